@@ -1,0 +1,177 @@
+"""Benchmark of one wide-batch latent-MoE decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--tokens 256] [--zipf]
+                    [--no-cpu-baseline] [--sweep]
+
+A step is one moe_layer call (router GEMM, sigmoid top-16, lists and unit windows,
+latent down, MXFP8 latent, grouped MXFP4 x MXFP8 experts, Finalize, RMSNorm, shared
+expert, up-projection add) over T tokens of synthetic input resident in HBM: hidden
+7168, latent 3584, 896 experts, top-16, expert intermediate 512, shared intermediate
+6144.  Prints one JSON line: tokens/s, the layer's HBM-roofline fraction over the weight
+bytes it must stream (dense + each touched expert once), the grouped-FFN kernel's
+roofline (HIP events on the launch stream), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+DENSE_BYTES = 379_857_408          # router + shared gate_up + shared down + latent down + up + norm + bias
+EXPERT_BYTES = 2_924_544           # one MXFP4 expert: W13 + scales + W2 + scales
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--tokens", type=int, default=256)
+    p.add_argument("--zipf", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=160)
+    p.add_argument("--sweep", action="store_true", help="also time T in {65,130,255,510,1020}")
+    return p.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer runs at TP1 on a single MI355X; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_synth as syn
+    import mixture_experts_decode_gemm_amd as moe
+
+    moe.lib()  # raises when the HIP library is not built: there is no fallback
+    T = a.tokens
+    d0 = syn.full_dims(T)
+    t0 = time.time()
+    w = syn.layer_weights(d0, seed=0)
+    if a.zipf:
+        w["bias"] = syn.routing_bias(896, 1, True)
+    x = syn.layer_input(syn.full_dims(1020), seed=1)  # the widest batch; the first T rows are used
+
+    def dev(arr):
+        arr = np.ascontiguousarray(arr)
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(arr).cuda()
+
+    dw = {k: dev(v) for k, v in w.items() if v is not None}
+    xd = dev(x)
+    print(f"# inputs generated and resident in HBM in {time.time() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    lw = moe.layer_weights(dw["w_gate"], dw["bias"], dw["w_down"], dw["w_shared_gu"],
+                           dw["w_shared_dn"], dw["norm_w"], dw["w_up"], dw["w13"], dw["s13"],
+                           dw["w2"], dw["s2"])
+    dmax = moe.dims(1020, 1020)
+    ws = torch.zeros(moe.moe_workspace_size(dmax), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run_T(t, steps, warmup):
+        d = moe.dims(t, 1020)
+        xin = xd[:t].contiguous()
+        out = torch.empty(t, 7168, dtype=torch.bfloat16, device="cuda")
+        for _ in range(warmup):
+            moe.moe_layer(d, lw, xin, out, ws, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            moe.moe_layer(d, lw, xin, out, ws, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        v = moe.workspace_views(d, ws)
+        D = int(torch.count_nonzero(v["counts"]).item())
+        nu = int(v["num_units"][0].item())
+        return ms, D, nu, d, v
+
+    ms, D, nu, d, v = run_T(T, a.steps, a.warmup)
+    layer_bytes = DENSE_BYTES + D * EXPERT_BYTES
+    layer_gbs = layer_bytes / (ms * 1e-3) / 1e9
+    print(f"# T={T}: {ms * 1e3:.1f} us/layer, D={D} touched experts, {nu} units, "
+          f"{layer_gbs:.0f} GB/s = {100 * layer_gbs / HBM_PEAK_GBS:.1f}% of HBM", file=sys.stderr,
+          flush=True)
+
+    # the dominant kernel: the grouped expert FFN (its two launches, up and down) timed with
+    # HIP events on its launch stream, fed the layer's own codes, lists and units
+    rows = torch.empty(T * 16, 3584, dtype=torch.bfloat16, device="cuda")
+    fws = torch.empty(moe.moe_ffn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    units = v["units_raw"]
+    ffn_args = (d, dw["w13"], dw["s13"], dw["w2"], dw["s2"], v["codes"], v["scales"], v["pairs"],
+                units, v["num_units"], rows, fws)
+    for _ in range(3):
+        moe.moe_grouped_ffn(*ffn_args, stream=stream)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(a.steps):
+        moe.moe_grouped_ffn(*ffn_args, stream=stream)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ffn_ms = f0.elapsed_time(f1) / a.steps
+    # algorithmic bytes of one grouped-FFN call: each touched expert's MXFP4 weights once,
+    # the MXFP8 latent (codes + scales) once, the BF16 expanded rows written once
+    ffn_bytes = D * EXPERT_BYTES + T * 3584 * 33 // 32 + T * 16 * 3584 * 2
+    ffn_gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "MoE-layer decode tokens/s at 256 tokens; % of HBM roofline (GB/s achieved)",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+mxfp4xmxfp8",
+        "data": "synthetic (seeded; random-init weights of the layer's shapes)",
+        "config": {"workload": f"wide latent-MoE decode layer, T={T} tokens, hidden 7168, latent "
+                               f"3584, 896 MXFP4 experts top-16, expert inter 512, shared inter "
+                               f"6144, {'Zipf' if a.zipf else 'uniform'} routing bias",
+                   "tokens": T, "touched_experts": D, "units": nu},
+        "layer_roofline": {"bound": "hbm", "weight_bytes": layer_bytes,
+                           "achieved": layer_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": layer_gbs / HBM_PEAK_GBS},
+        "roofline": {"kernel": "moe_grouped_ffn (k_ffn_up_mx + k_ffn_down_mx)", "bound": "hbm",
+                     "achieved": ffn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ffn_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": ffn_bytes, "us_per_launch": ffn_ms * 1e3},
+    }
+    if a.sweep:
+        sweep = {}
+        for t in (65, 130, 255, 510, 1020):
+            m, Dt, nut, _, _ = run_T(t, max(5, a.steps // 2), 3)
+            bt = DENSE_BYTES + Dt * EXPERT_BYTES
+            sweep[str(t)] = {"us": m * 1e3, "tokens_per_s": t / (m * 1e-3), "D": Dt, "units": nut,
+                             "gbs": bt / (m * 1e-3) / 1e9,
+                             "hbm_frac": bt / (m * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            print(f"# sweep T={t}: {m * 1e3:.1f} us", file=sys.stderr, flush=True)
+        res["sweep"] = sweep
+    if not a.no_cpu_baseline:
+        import oracle as orc
+        n = a.cpu_tokens
+        sub = np.arange(n)
+        dsub = dict(d0, T=n)
+        orc.lib()
+        c0 = time.time()
+        orc.layer(dsub, w, x[sub])
+        sec = time.time() - c0
+        res["cpu_baseline"] = {"value": n / sec, "unit": "tokens/s", "cores": orc.threads(),
+                               "kind": "oracle",
+                               "sample": f"the oracle layer on the first {n} of the {T} tokens "
+                                         f"(same weights and inputs), {sec:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

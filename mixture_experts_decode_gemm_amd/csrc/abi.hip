@@ -1,0 +1,316 @@
+// abi.hip -- the C ABI of libmoedecode (include/moedecode.h): host-side argument
+// checks, workspace layout, and the layer's launch sequence on one stream.
+// Nothing here allocates, frees or synchronises.
+#include <string.h>
+
+#include "../../include/moedecode.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxTokens = 4096;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t up256(size_t b) { return (b + 255) / 256 * 256; }
+
+moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// checks shared by every call that takes moe_dims
+moe_status check_dims(const moe_dims* d) {
+    if (!d) return MOE_ERR_NULL;
+    if (d->tokens < 1 || d->max_tokens < d->tokens || d->max_tokens > kMaxTokens)
+        return MOE_ERR_SHAPE;
+    if (d->hidden < 64 || d->hidden % 64 || d->latent < 64 || d->latent % 64) return MOE_ERR_SHAPE;
+    if (d->shared_inter < 64 || d->shared_inter % 64) return MOE_ERR_SHAPE;
+    if (d->experts < 1 || d->experts > kMaxExperts) return MOE_ERR_SHAPE;
+    if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->experts) return MOE_ERR_SHAPE;
+    if (d->unit_tokens != 8 && d->unit_tokens != 16) return MOE_ERR_SHAPE;
+    if (d->expert_inter < 32 || d->expert_inter % 32) return MOE_ERR_SHAPE;
+    if (!(d->rms_eps >= 0.0f)) return MOE_ERR_SHAPE;
+    if (d->expert_format == MOE_FMT_MXFP4_MXFP8) {
+        if (d->latent % 256 || d->expert_inter % 128) return MOE_ERR_SHAPE;
+    } else if (d->expert_format == MOE_FMT_BF16) {
+        if (d->expert_inter > 4096) return MOE_ERR_SHAPE;
+    } else {
+        return MOE_ERR_FORMAT;
+    }
+    return MOE_OK;
+}
+
+struct Layout {
+    size_t off[MOE_WS_FIELDS];
+    size_t gu, act, uni, total;
+};
+
+Layout layout(const moe_dims* d) {
+    const size_t T = d->max_tokens, H = d->hidden, L = d->latent, E = d->experts, K = d->top_k;
+    const size_t S = d->shared_inter, P = T * K;
+    const size_t U = (P + d->unit_tokens - 1) / d->unit_tokens + E;
+    const size_t I = d->expert_inter;
+    const size_t sizes[17] = {T * E * 4, P * 4, P * 4, E * 4, (E + 1) * 4, P * 4, U * 16, 16,
+                              T * L * 2, T * L, T * (L / 32), P * L * 2, T * L * 2, T * H * 2,
+                              T * L * 2, P * I, P * (I / 32)};
+    Layout lo;
+    size_t at = 0;
+    for (int i = 0; i < 17; ++i) {
+        lo.off[i] = at;
+        at += up256(sizes[i]);
+    }
+    lo.off[17] = at;
+    lo.gu = at;
+    at += up256(T * 2 * S * 2);
+    lo.act = at;
+    at += up256(T * S * 2);
+    lo.uni = at;
+    const int Tm = d->max_tokens;
+    size_t u = 0;
+    const size_t g[5] = {gemm_scratch_bytes(Tm, d->experts, d->hidden),
+                         gemm_scratch_bytes(Tm, d->latent, d->hidden),
+                         gemm_scratch_bytes(Tm, 2 * d->shared_inter, d->hidden),
+                         gemm_scratch_bytes(Tm, d->hidden, d->shared_inter),
+                         gemm_scratch_bytes(Tm, d->hidden, d->latent)};
+    for (size_t v : g) u = v > u ? v : u;
+    const size_t ls = lists_scratch_bytes(Tm, d->experts);
+    u = ls > u ? ls : u;
+    lo.total = at + up256(u);
+    return lo;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "libmoedecode 0.1 (gfx950)"; }
+
+size_t moe_router_workspace_size(const moe_dims* d) {
+    if (check_dims(d) != MOE_OK) return 0;
+    return gemm_scratch_bytes(d->max_tokens, d->experts, d->hidden);
+}
+
+moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
+                           const float* bias, float* logits, int32_t* ids, float* weights,
+                           int32_t flags, void* workspace, size_t ws_bytes, void* stream) {
+    moe_status st = check_dims(d);
+    if (st != MOE_OK) return st;
+    if (flags & ~MOE_LOGITS_GIVEN) return MOE_ERR_FORMAT;
+    const bool given = flags & MOE_LOGITS_GIVEN;
+    if (!bias || !logits || !ids || !weights) return MOE_ERR_NULL;
+    if (!given && (!x || !w_gate)) return MOE_ERR_NULL;
+    if (!al16(bias) || !al16(logits) || !al16(ids) || !al16(weights)) return MOE_ERR_ALIGN;
+    if (!given && (!al16(x) || !al16(w_gate))) return MOE_ERR_ALIGN;
+    const size_t need = given ? 0 : gemm_scratch_bytes(d->tokens, d->experts, d->hidden);
+    if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+    if (workspace && !al16(workspace)) return MOE_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (!given) {
+        hipError_t e = launch_gemm(d->tokens, d->experts, d->hidden, x, w_gate, logits, nullptr, 0,
+                                   workspace, s);
+        if (e != hipSuccess) return MOE_ERR_LAUNCH;
+    }
+    return launch_status(launch_topk(d->tokens, d->experts, d->top_k, logits, bias,
+                                     d->renormalize, d->routed_scale, ids, weights, s));
+}
+
+size_t moe_lists_workspace_size(const moe_dims* d) {
+    if (check_dims(d) != MOE_OK) return 0;
+    return lists_scratch_bytes(d->max_tokens, d->experts);
+}
+
+moe_status moe_build_lists(const moe_dims* d, const int32_t* ids, int32_t* counts,
+                           int32_t* offsets, int32_t* pairs, moe_unit* units,
+                           int32_t* num_units, void* workspace, size_t ws_bytes, void* stream) {
+    moe_status st = check_dims(d);
+    if (st != MOE_OK) return st;
+    if (!ids || !counts || !offsets || !pairs || !units || !num_units || !workspace)
+        return MOE_ERR_NULL;
+    if (!al16(ids) || !al16(counts) || !al16(offsets) || !al16(pairs) || !al16(units) ||
+        !al16(num_units) || !al16(workspace))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < lists_scratch_bytes(d->tokens, d->experts)) return MOE_ERR_WORKSPACE;
+    return launch_status(launch_lists(d->tokens, d->top_k, d->experts, d->unit_tokens, ids, counts,
+                                      offsets, pairs, (int32_t*)units, num_units, workspace,
+                                      (hipStream_t)stream));
+}
+
+moe_status moe_quant_mxfp8(int32_t rows, int32_t cols, const void* x, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+    if (rows < 1 || cols < 32 || cols % 32 || (long)rows * cols > (1L << 34)) return MOE_ERR_SHAPE;
+    if (!x || !codes || !scales) return MOE_ERR_NULL;
+    if (!al16(x) || !al16(codes) || !al16(scales)) return MOE_ERR_ALIGN;
+    return launch_status(launch_quant_mxfp8(rows, cols, x, codes, scales, (hipStream_t)stream));
+}
+
+size_t moe_ffn_workspace_size(const moe_dims* d) {
+    if (check_dims(d) != MOE_OK) return 0;
+    if (d->expert_format == MOE_FMT_BF16) return 256;
+    return ffn_scratch_bytes(d->max_tokens * d->top_k, d->expert_inter);
+}
+
+moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const void* act,
+                           const uint8_t* act_scales, const int32_t* pairs,
+                           const moe_unit* units, const int32_t* num_units, void* rows,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    moe_status st = check_dims(d);
+    if (st != MOE_OK) return st;
+    if (!w || !w->w13 || !w->w2 || !act || !pairs || !units || !num_units || !rows)
+        return MOE_ERR_NULL;
+    const bool mx = d->expert_format == MOE_FMT_MXFP4_MXFP8;
+    if (mx && (!w->s13 || !w->s2 || !act_scales || !workspace)) return MOE_ERR_NULL;
+    if (!al16(w->w13) || !al16(w->w2) || !al16(act) || !al16(pairs) || !al16(units) ||
+        !al16(num_units) || !al16(rows))
+        return MOE_ERR_ALIGN;
+    if (mx && (!al16(w->s13) || !al16(w->s2) || !al16(act_scales) || !al16(workspace)))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (mx) {
+        if (ws_bytes < ffn_scratch_bytes(d->tokens * d->top_k, d->expert_inter))
+            return MOE_ERR_WORKSPACE;
+        uint8_t* hid = (uint8_t*)workspace;
+        uint8_t* hsc = hid + up256((size_t)d->tokens * d->top_k * d->expert_inter);
+        return launch_status(launch_ffn_mx(
+            d->tokens, d->top_k, d->experts, d->latent, d->expert_inter, d->unit_tokens,
+            (const uint8_t*)w->w13, (const uint8_t*)w->s13, (const uint8_t*)w->w2,
+            (const uint8_t*)w->s2, (const uint8_t*)act, act_scales, pairs, (const int32_t*)units,
+            num_units, rows, hid, hsc, s));
+    }
+    return launch_status(launch_ffn_bf16(d->tokens, d->top_k, d->experts, d->latent,
+                                         d->expert_inter, d->unit_tokens, w->w13, w->w2, act,
+                                         pairs, (const int32_t*)units, num_units, rows, s));
+}
+
+moe_status moe_finalize(int32_t tokens, int32_t top_k, int32_t cols, const void* rows,
+                        const float* weights, const int32_t* ids, void* out, void* stream) {
+    if (tokens < 1 || top_k < 1 || top_k > kMaxTopK || cols < 8 || cols % 8) return MOE_ERR_SHAPE;
+    if ((long)tokens * (cols / 8) >= (1L << 31) - 256) return MOE_ERR_SHAPE;
+    if (!rows || !weights || !out) return MOE_ERR_NULL;
+    if (!al16(rows) || !al16(weights) || !al16(out) || (ids && !al16(ids))) return MOE_ERR_ALIGN;
+    return launch_status(
+        launch_finalize(tokens, top_k, cols, rows, weights, ids, out, (hipStream_t)stream));
+}
+
+moe_status moe_rmsnorm(int32_t rows, int32_t cols, const void* r, const void* g, float eps,
+                       void* out, void* stream) {
+    if (rows < 1 || cols < 8 || cols % 8 || !(eps >= 0.0f)) return MOE_ERR_SHAPE;
+    if (!r || !g || !out) return MOE_ERR_NULL;
+    if (!al16(r) || !al16(g) || !al16(out)) return MOE_ERR_ALIGN;
+    return launch_status(launch_rmsnorm(rows, cols, r, g, eps, out, (hipStream_t)stream));
+}
+
+size_t moe_linear_workspace_size(int32_t M, int32_t N, int32_t K) {
+    if (M < 1 || N < 1 || K < 64 || K % 64) return 0;
+    return gemm_scratch_bytes(M, N, K);
+}
+
+moe_status moe_linear(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* out,
+                      const void* add, int32_t mode, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    if (M < 1 || M > 65536 || N < 1 || N > (1 << 20) || K < 64 || K % 64) return MOE_ERR_SHAPE;
+    if (mode < MOE_LINEAR_F32 || mode > MOE_LINEAR_ADD_BF16) return MOE_ERR_FORMAT;
+    if (!x || !w || !out || (mode == MOE_LINEAR_ADD_BF16 && !add)) return MOE_ERR_NULL;
+    if (!al16(x) || !al16(w) || !al16(out) || (add && !al16(add))) return MOE_ERR_ALIGN;
+    const size_t need = gemm_scratch_bytes(M, N, K);
+    if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+    if (workspace && !al16(workspace)) return MOE_ERR_ALIGN;
+    return launch_status(launch_gemm(M, N, K, x, w, out, add, mode, workspace, (hipStream_t)stream));
+}
+
+moe_status moe_silu_mul(int32_t M, int32_t S, const void* gu, void* out, void* stream) {
+    if (M < 1 || S < 8 || S % 8) return MOE_ERR_SHAPE;
+    if (!gu || !out) return MOE_ERR_NULL;
+    if (!al16(gu) || !al16(out)) return MOE_ERR_ALIGN;
+    return launch_status(launch_silu_mul(M, S, gu, out, (hipStream_t)stream));
+}
+
+size_t moe_workspace_size(const moe_dims* d) {
+    if (check_dims(d) != MOE_OK) return 0;
+    return layout(d).total;
+}
+
+moe_status moe_workspace_layout(const moe_dims* d, size_t offsets[MOE_WS_FIELDS]) {
+    moe_status st = check_dims(d);
+    if (st != MOE_OK) return st;
+    if (!offsets) return MOE_ERR_NULL;
+    const Layout lo = layout(d);
+    memcpy(offsets, lo.off, sizeof(lo.off));
+    return MOE_OK;
+}
+
+moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* x, void* out,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    moe_status st = check_dims(d);
+    if (st != MOE_OK) return st;
+    if (!w || !x || !out || !workspace) return MOE_ERR_NULL;
+    if (!w->w_gate || !w->bias || !w->w_down || !w->w_shared_gu || !w->w_shared_down ||
+        !w->norm_w || !w->w_up || !w->experts.w13 || !w->experts.w2)
+        return MOE_ERR_NULL;
+    const bool mx = d->expert_format == MOE_FMT_MXFP4_MXFP8;
+    if (mx && (!w->experts.s13 || !w->experts.s2)) return MOE_ERR_NULL;
+    const void* ptrs[] = {w->w_gate, w->bias, w->w_down, w->w_shared_gu, w->w_shared_down,
+                          w->norm_w, w->w_up, w->experts.w13, w->experts.w2, x, out, workspace};
+    for (const void* p : ptrs)
+        if (!al16(p)) return MOE_ERR_ALIGN;
+    if (mx && (!al16(w->experts.s13) || !al16(w->experts.s2))) return MOE_ERR_ALIGN;
+    const Layout lo = layout(d);
+    if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE;
+
+    char* ws = (char*)workspace;
+    float* logits = (float*)(ws + lo.off[0]);
+    int32_t* ids = (int32_t*)(ws + lo.off[1]);
+    float* wts = (float*)(ws + lo.off[2]);
+    int32_t* counts = (int32_t*)(ws + lo.off[3]);
+    int32_t* offs = (int32_t*)(ws + lo.off[4]);
+    int32_t* pairs = (int32_t*)(ws + lo.off[5]);
+    int32_t* units = (int32_t*)(ws + lo.off[6]);
+    int32_t* nu = (int32_t*)(ws + lo.off[7]);
+    void* latent = ws + lo.off[8];
+    uint8_t* codes = (uint8_t*)(ws + lo.off[9]);
+    uint8_t* scales = (uint8_t*)(ws + lo.off[10]);
+    void* rows = ws + lo.off[11];
+    void* routed = ws + lo.off[12];
+    void* shared = ws + lo.off[13];
+    void* normed = ws + lo.off[14];
+    uint8_t* hid = (uint8_t*)(ws + lo.off[15]);
+    uint8_t* hid_scales = (uint8_t*)(ws + lo.off[16]);
+    void* gu = ws + lo.gu;
+    void* act = ws + lo.act;
+    void* uni = ws + lo.uni;
+
+    const int T = d->tokens, H = d->hidden, L = d->latent, E = d->experts, K = d->top_k;
+    const int S = d->shared_inter, I = d->expert_inter;
+    hipStream_t s = (hipStream_t)stream;
+#define MOE_TRY(call)                                   \
+    do {                                                \
+        if ((call) != hipSuccess) return MOE_ERR_LAUNCH; \
+    } while (0)
+    // routing: FP32 router GEMM, sigmoid top-K, lists and unit windows
+    MOE_TRY(launch_gemm(T, E, H, x, w->w_gate, logits, nullptr, 0, uni, s));
+    MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts, s));
+    MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, s));
+    // latent down (one BF16 rounding), MXFP8 latent, grouped experts, Finalize
+    MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s));
+    if (mx) {
+        MOE_TRY(launch_quant_mxfp8(T, L, latent, codes, scales, s));
+        MOE_TRY(launch_ffn_mx(T, K, E, L, I, d->unit_tokens, (const uint8_t*)w->experts.w13,
+                              (const uint8_t*)w->experts.s13, (const uint8_t*)w->experts.w2,
+                              (const uint8_t*)w->experts.s2, codes, scales, pairs, units, nu,
+                              rows, hid, hid_scales, s));
+    } else {
+        MOE_TRY(launch_ffn_bf16(T, K, E, L, I, d->unit_tokens, w->experts.w13, w->experts.w2,
+                                latent, pairs, units, nu, rows, s));
+    }
+    MOE_TRY(launch_finalize(T, K, L, rows, wts, nullptr, routed, s));
+    MOE_TRY(launch_rmsnorm(T, L, routed, w->norm_w, d->rms_eps, normed, s));
+    // shared expert, then the up-projection added into the shared partial (one rounding)
+    MOE_TRY(launch_gemm(T, 2 * S, H, x, w->w_shared_gu, gu, nullptr, 1, uni, s));
+    MOE_TRY(launch_silu_mul(T, S, gu, act, s));
+    MOE_TRY(launch_gemm(T, H, S, act, w->w_shared_down, shared, nullptr, 1, uni, s));
+    MOE_TRY(launch_gemm(T, H, L, normed, w->w_up, out, shared, 2, uni, s));
+#undef MOE_TRY
+    return MOE_OK;
+}
+
+}  // extern "C"

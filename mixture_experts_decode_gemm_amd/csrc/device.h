@@ -1,0 +1,77 @@
+// device.h -- small device helpers shared by the libmoedecode kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int WAVE = 64;
+
+// ---- BF16 -------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round-to-nearest-even FP32 -> BF16 bits (NaN -> quiet NaN; overflow -> inf)
+__device__ __forceinline__ uint32_t f_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f_to_bf16(lo) | (f_to_bf16(hi) << 16);
+}
+
+// ---- MXFP8 (OCP MX: E4M3 elements, E8M0 block scale) --------------------------------
+// floor(log2 |v|) of a nonzero finite FP32 magnitude given as bits (subnormals included)
+__device__ __forceinline__ int ilog2_f32_bits(uint32_t mag) {
+    int e = (int)(mag >> 23);
+    if (e) return e - 127;
+    return (31 - __clz((int)mag)) - 149;
+}
+
+// block exponent X = floor(log2 amax) - 8 (8 = largest E4M3 exponent), clamped to the
+// E8M0 range; the all-zero block returns the smallest scale (byte 0)
+__device__ __forceinline__ int mx_block_exponent(uint32_t amax_f32_bits) {
+    if (amax_f32_bits == 0) return -127;
+    int x = ilog2_f32_bits(amax_f32_bits) - 8;
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// E4M3 code of v (already divided by the block scale): round to nearest even,
+// saturating to +-448, the sign of zero kept.  v is finite.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t mag = u & 0x7FFFFFFFu;
+    float a = __uint_as_float(mag);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (mag < 0x3C800000u) {  // a < 2^-6: subnormal grid of step 2^-9
+        code = (uint32_t)rintf(a * 512.0f);  // 0..8 (8 = the smallest normal, 0x08)
+    } else {
+        uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);  // keep 3 mantissa bits, RNE
+        int e = (int)(r >> 23) - 127;
+        code = ((uint32_t)(e + 7) << 3) | ((r >> 20) & 7u);
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return sign | code;
+}
+
+// ---- wave helpers ---------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, off, WAVE);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+}  // namespace moe

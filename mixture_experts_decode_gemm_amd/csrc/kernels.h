@@ -1,0 +1,48 @@
+// kernels.h -- host-side launchers of the libmoedecode kernels (internal; the public
+// ABI is include/moedecode.h).  Every launcher only enqueues work on `stream` and
+// returns hipGetLastError().  Arguments are validated by the callers in abi.hip.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_finalize(int T, int K, int cols, const void* rows, const float* w,
+                           const int32_t* ids, void* out, hipStream_t s);
+
+hipError_t launch_quant_mxfp8(int rows, int cols, const void* x, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+
+hipError_t launch_topk(int T, int E, int K, const float* logits, const float* bias, int renorm,
+                       float scale, int32_t* ids, float* w, hipStream_t s);
+
+// routing lists: scratch of lists_scratch_bytes(T, E) bytes
+size_t lists_scratch_bytes(int T, int E);
+hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* pairs, int32_t* units, int32_t* num_units,
+                        void* scratch, hipStream_t s);
+
+// grouped FFN: MXFP4 x MXFP8; the MXFP8 hidden goes to hid [T*K, I] and hid_scales
+// [T*K, I/32] (by pair id); ffn_scratch_bytes(P, I) covers both, 256-aligned
+size_t ffn_scratch_bytes(int P, int I);
+hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint8_t* w13,
+                         const uint8_t* s13, const uint8_t* w2, const uint8_t* s2,
+                         const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
+                         const int32_t* units, const int32_t* num_units, void* rows,
+                         uint8_t* hid, uint8_t* hid_scales, hipStream_t s);
+hipError_t launch_ffn_bf16(int T, int K, int E, int L, int I, int unit, const void* w13,
+                           const void* w2, const void* latent, const int32_t* pairs,
+                           const int32_t* units, const int32_t* num_units, void* rows,
+                           hipStream_t s);
+
+// dense BF16 GEMM out = x W^T (mode 0 FP32 out, 1 BF16 out, 2 BF16 out with BF16 add)
+size_t gemm_scratch_bytes(int M, int N, int K);
+hipError_t launch_gemm(int M, int N, int K, const void* x, const void* w, void* out,
+                       const void* add, int mode, void* scratch, hipStream_t s);
+
+hipError_t launch_rmsnorm(int rows, int cols, const void* r, const void* g, float eps, void* out,
+                          hipStream_t s);
+hipError_t launch_silu_mul(int M, int S, const void* gu, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,140 @@
+// lists.hip -- per-expert routing lists and unit windows (wide page, WideRoute: each
+// (token, slot) pair appended to its expert's list as token*K + slot; module summary:
+// unit windows of 8 tokens per touched expert).
+//
+// The pages claim list slots with relaxed atomic counters, so a list's order depends on
+// timing.  Here the build is deterministic, in three small launches:
+//   mark  -- one workgroup per 32-token column w: bm[w][e] = bitmask of the column's
+//            tokens that chose expert e (LDS bit-ORs, whose result is order-free; an id
+//            outside [0,E) sets nothing, a repeated id sets the same bit once);
+//   scan  -- one workgroup, one thread per expert: counts, per-word running offsets,
+//            exclusive prefix sums over experts (offsets, unit bases), the units;
+//   fill  -- one thread per (word, expert): the set bits in ascending token order give
+//            the list entries; the slot k is the first slot of that token holding e.
+// Lists therefore hold ascending pair ids, and units run over experts ascending.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+size_t lists_scratch_bytes(int T, int E) {
+    const size_t W = (size_t)(T + 31) / 32;
+    return 2 * W * (size_t)E * sizeof(uint32_t);
+}
+
+__global__ __launch_bounds__(256) void k_lists_mark(int T, int K, int E,
+                                                    const int32_t* __restrict__ ids,
+                                                    uint32_t* __restrict__ bm) {
+    __shared__ uint32_t words[1024];
+    const int w = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += 256) words[e] = 0;
+    __syncthreads();
+    const int t0 = w * 32;
+    const int n = min(32, T - t0) * K;
+    for (int q = threadIdx.x; q < n; q += 256) {
+        const int e = ids[(size_t)t0 * K + q];
+        if (e >= 0 && e < E) atomicOr(&words[e], 1u << (q / K));
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) bm[(size_t)w * E + e] = words[e];
+}
+
+// exclusive prefix sum over a 1024-thread block; returns the total through *total
+__device__ int block_exclusive_scan_1024(int v, int* smem, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) smem[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < 16; ++i) {
+            const int c = smem[i];
+            smem[i] = run;
+            run += c;
+        }
+        smem[16] = run;
+    }
+    __syncthreads();
+    const int res = smem[wave] + x - v;
+    *total = smem[16];
+    __syncthreads();
+    return res;
+}
+
+__global__ __launch_bounds__(1024) void k_lists_scan(int T, int K, int E, int unit,
+                                                     const uint32_t* __restrict__ bm,
+                                                     int32_t* __restrict__ wordoff,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int4* __restrict__ units,
+                                                     int32_t* __restrict__ num_units) {
+    __shared__ int smem[17];
+    const int W = (T + 31) / 32;
+    const int e = threadIdx.x;
+    int c = 0;
+    if (e < E)
+        for (int w = 0; w < W; ++w) {
+            wordoff[(size_t)w * E + e] = c;
+            c += __popc(bm[(size_t)w * E + e]);
+        }
+    int total_pairs, total_units;
+    const int off = block_exclusive_scan_1024(c, smem, &total_pairs);
+    const int nu = (c + unit - 1) / unit;
+    const int ub = block_exclusive_scan_1024(nu, smem, &total_units);
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = off;
+        for (int w = 0; w < W; ++w) wordoff[(size_t)w * E + e] += off;
+        for (int j = 0; j < nu; ++j) {
+            const int rest = c - j * unit;
+            units[ub + j] = make_int4(e, off + j * unit, rest < unit ? rest : unit, 0);
+        }
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = total_pairs;
+        num_units[0] = total_units;
+        num_units[1] = T * K - total_pairs;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
+                                                    const int32_t* __restrict__ ids,
+                                                    const uint32_t* __restrict__ bm,
+                                                    const int32_t* __restrict__ wordoff,
+                                                    int32_t* __restrict__ pairs) {
+    const int W = (T + 31) / 32;
+    const int gid = blockIdx.x * 256 + threadIdx.x;
+    if (gid >= W * E) return;
+    const int w = gid / E, e = gid - w * E;
+    uint32_t word = bm[gid];
+    int pos = wordoff[gid];
+    while (word) {
+        const int j = __ffs((int)word) - 1;
+        word &= word - 1;
+        const int t = w * 32 + j;
+        int k = 0;
+        while (ids[(size_t)t * K + k] != e) ++k;  // the bit guarantees a match
+        pairs[pos++] = t * K + k;
+    }
+}
+
+hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* pairs, int32_t* units, int32_t* num_units,
+                        void* scratch, hipStream_t s) {
+    const int W = (T + 31) / 32;
+    uint32_t* bm = (uint32_t*)scratch;
+    int32_t* wordoff = (int32_t*)(bm + (size_t)W * E);
+    hipLaunchKernelGGL(k_lists_mark, dim3(W), dim3(256), 0, s, T, K, E, ids, bm);
+    hipLaunchKernelGGL(k_lists_scan, dim3(1), dim3(1024), 0, s, T, K, E, unit, bm, wordoff,
+                       counts, offsets, (int4*)units, num_units);
+    hipLaunchKernelGGL(k_lists_fill, dim3((W * E + 255) / 256), dim3(256), 0, s, T, K, E, ids, bm,
+                       wordoff, pairs);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,81 @@
+// norm.hip -- latent RMSNorm (ep/layer page, EpMoeLayer: ops.rms_norm(normed, routed,
+// norm, eps); wide page, WideMoE.tail: the RMSNorm fused into the latent all-reduce) and
+// the shared expert's gated activation (ep/layer page, EpMoeLayer.gate_up: the [T, 2S]
+// gate_up rows; SiLU-and-mul stands in for the pages' undefined "SiTU").
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+// one workgroup of 256 threads per row; 16-byte loads; FP32 sum of squares reduced
+// across the wavefront by xor shuffles and across the four wavefronts in LDS
+__global__ __launch_bounds__(256) void k_rmsnorm(int cols8, const uint4* __restrict__ r,
+                                                 const uint4* __restrict__ g, float eps,
+                                                 uint4* __restrict__ out) {
+    __shared__ float part[4];
+    const int row = blockIdx.x;
+    const uint4* src = r + (size_t)row * cols8;
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < cols8; c += 256) {
+        const uint4 v = src[c];
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = bf16_lo(q[i]), b = bf16_hi(q[i]);
+            ss = __builtin_fmaf(a, a, ss);
+            ss = __builtin_fmaf(b, b, ss);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = 1.0f / sqrtf(tot / (float)(cols8 * 8) + eps);
+    for (int c = threadIdx.x; c < cols8; c += 256) {
+        const uint4 v = src[c], gw = g[c];
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t h[4] = {gw.x, gw.y, gw.z, gw.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = pack_bf16x2(bf16_lo(q[i]) * inv * bf16_lo(h[i]),
+                               bf16_hi(q[i]) * inv * bf16_hi(h[i]));
+        out[(size_t)row * cols8 + c] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+hipError_t launch_rmsnorm(int rows, int cols, const void* r, const void* g, float eps, void* out,
+                          hipStream_t s) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(rows), dim3(256), 0, s, cols / 8, (const uint4*)r,
+                       (const uint4*)g, eps, (uint4*)out);
+    return hipGetLastError();
+}
+
+// out[m, j] = BF16(silu(gu[m, j]) * gu[m, S + j]); one thread per 8 columns
+__global__ __launch_bounds__(256) void k_silu_mul(int M, int S8, const uint4* __restrict__ gu,
+                                                  uint4* __restrict__ out) {
+    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (long)M * S8) return;
+    const long m = gid / S8, c = gid - m * S8;
+    const uint4 gv = gu[m * 2 * S8 + c], uv = gu[m * 2 * S8 + S8 + c];
+    const uint32_t gq[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uq[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float g0 = bf16_lo(gq[i]), g1 = bf16_hi(gq[i]);
+        o[i] = pack_bf16x2(g0 / (1.0f + __expf(-g0)) * bf16_lo(uq[i]),
+                           g1 / (1.0f + __expf(-g1)) * bf16_hi(uq[i]));
+    }
+    out[gid] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_silu_mul(int M, int S, const void* gu, void* out, hipStream_t s) {
+    const long n = (long)M * (S / 8);
+    hipLaunchKernelGGL(k_silu_mul, dim3((int)((n + 255) / 256)), dim3(256), 0, s, M, S / 8,
+                       (const uint4*)gu, (uint4*)out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

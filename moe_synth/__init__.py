@@ -9,6 +9,9 @@ the method runs here.  BF16 tensors are numpy ``uint16`` bit patterns.
 Every tensor has its own Philox stream keyed by (seed, tensor id[, expert]), so any
 tensor or any single expert can be regenerated on its own.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 # tensor ids of the independent streams
@@ -63,6 +66,18 @@ def mxfp4_random(g, rows, cols, std):
     return packed, scales
 
 
+def mxfp8_random(g, rows, cols):
+    """MXFP8 activation bytes drawn directly: E4M3 codes with a uniform sign and mantissa
+    and an exponent field 2 + (sum of four 2-bit draws) in [2, 14] (never the NaN code),
+    and E8M0 scale bytes 120 or 121 (about the scale of an N(0,1) block)."""
+    r = np.frombuffer(g.bytes(rows * cols * 2), dtype=np.uint8).reshape(2, rows * cols)
+    b = r[1]
+    ex = 2 + (b & 3) + ((b >> 2) & 3) + ((b >> 4) & 3) + ((b >> 6) & 3)
+    codes = ((r[0] & 0x80) | (ex.astype(np.uint8) << 3) | (r[0] & 7)).astype(np.uint8)
+    scales = (np.uint8(120) + g.integers(0, 2, size=(rows, cols // 32), dtype=np.uint8))
+    return codes.reshape(rows, cols), scales.astype(np.uint8)
+
+
 def layer_weights(d, seed=0, zipf=False, bias_seed=None, experts=True):
     """All weights of one layer.  Dense weights BF16 N(0, 1/sqrt(fan_in)); router
     bias FP32 N(0, 0.05) (toy: 0.01) or, with zipf, 0.5*(r+1)^-1.1 over a seeded
@@ -98,9 +113,13 @@ def expert_weights(d, seed=0, only=None):
     s13 = np.zeros((E, 2 * I, L // 32), np.uint8)
     w2 = np.zeros((E, L, I // 2), np.uint8)
     s2 = np.zeros((E, L, I // 32), np.uint8)
-    for e in (range(E) if only is None else only):
+
+    def one(e):  # each expert has its own streams: the result is thread-order free
         w13[e], s13[e] = mxfp4_random(rng(seed, _W13, e), 2 * I, L, 1 / np.sqrt(L))
         w2[e], s2[e] = mxfp4_random(rng(seed, _W2, e), L, I, 1 / np.sqrt(I))
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, range(E) if only is None else only))
     return dict(w13=w13, s13=s13, w2=w2, s2=s2)
 
 

@@ -1,0 +1,110 @@
+"""GPU parity of the grouped expert FFN (MXFP4 weights x MXFP8 activations with the
+MXFP8 hidden; and the BF16-weight variant) against the oracle: hidden codes
+(teacher-forced on identical MXFP8 inputs; bit-exact except where FP32 accumulation
+order moves a value across a rounding boundary), expanded rows (tolerance; with the
+oracle's second half fed the GPU's hidden codes, and free-running), at small ragged
+shapes and at the full latent/intermediate sizes with multi-unit experts."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as syn
+import mixture_experts_decode_gemm_amd as moe
+from gpu_util import assert_close, assert_close_bf16, check_hidden, dev, f32, host, say
+
+pytestmark = pytest.mark.gpu
+
+def build_lists(d, ids_dev):
+    T, K, E = d.tokens, d.top_k, d.experts
+    P = T * K
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pairs = torch.empty(P, dtype=torch.int32, device="cuda")
+    units = torch.empty(-(-P // d.unit_tokens) + E, 4, dtype=torch.int32, device="cuda")
+    nu = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_lists_workspace_size(d), dtype=torch.uint8, device="cuda")
+    moe.moe_build_lists(d, ids_dev, counts, offsets, pairs, units, nu, ws)
+    return pairs, units, nu
+
+
+def run_ffn_mx(d, w, codes, scales, ids):
+    T, K, L, I = d.tokens, d.top_k, d.latent, d.expert_inter
+    ids_d = dev(ids)
+    pairs, units, nu = build_lists(d, ids_d)
+    rows = torch.zeros(T * K, L, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(moe.moe_ffn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_ffn(d, dev(w["w13"]), dev(w["s13"]), dev(w["w2"]), dev(w["s2"]), dev(codes),
+                        dev(scales), pairs, units, nu, rows, ws)
+    torch.cuda.synchronize()
+    P = T * K
+    hid = host(ws[:P * I]).reshape(P, I)
+    off = (P * I + 255) // 256 * 256
+    hsc = host(ws[off:off + P * (I // 32)]).reshape(P, I // 32)
+    return host(rows), hid, hsc
+
+
+def random_ids(g, T, K, E, hot=None):
+    ids = np.stack([g.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    if hot is not None:  # make expert `hot` appear in every token
+        for t in range(T):
+            if hot not in ids[t]:
+                ids[t, t % K] = hot
+    return ids
+
+
+def check_mx(orc, d, w, codes, scales, ids, sample):
+    T, K, I = d.tokens, d.top_k, d.expert_inter
+    rows, hid, hsc = run_ffn_mx(d, w, codes, scales, ids)
+    pexp = ids.reshape(-1)[sample]
+    hc, hs, hf = orc.ffn_up_mx(sample, pexp, K, codes, scales, w["w13"], w["s13"])
+    check_hidden(hid[sample], hsc[sample], hc, hs)
+    # second half teacher-forced on the GPU's hidden codes
+    ref_tf = orc.ffn_down_mx(pexp, hid[sample], hsc[sample], w["w2"], w["s2"])
+    assert_close_bf16(rows[sample], ref_tf, "rows (oracle fed GPU hidden)")
+    # free-running: a one-step hidden code flip is a correct outcome, so informational
+    ref = orc.ffn_down_mx(pexp, hc, hs, w["w2"], w["s2"])
+    assert_close(f32(rows[sample]), f32(ref), "rows (free-running oracle, sanity)", tol=0.1)
+
+
+@pytest.mark.parametrize("T,K,E,L,I,unit", [(16, 4, 8, 512, 128, 8), (13, 3, 5, 256, 256, 16),
+                                            (1, 1, 3, 256, 128, 8)])
+def test_ffn_mx_small(orc, T, K, E, L, I, unit):
+    say(f"ffn mx T={T} K={K} E={E} L={L} I={I} unit={unit}")
+    dd = dict(L=L, I=I, E=E, expert_format=0)
+    w = syn.expert_weights(dd, seed=T)
+    g = syn.rng(T, 700)
+    codes, scales = syn.mxfp8_random(g, T, L)
+    ids = random_ids(np.random.default_rng(T), T, K, E)
+    d = moe.dims(T, T, hidden=256, latent=L, experts=E, top_k=K, expert_inter=I,
+                 unit_tokens=unit)
+    check_mx(orc, d, w, codes, scales, ids, np.arange(T * K, dtype=np.int32))
+
+
+def test_ffn_mx_full_size_multi_unit(orc):
+    T, K, E, L, I = 256, 16, 64, 3584, 512
+    say(f"ffn mx full T={T} K={K} E={E} L={L} I={I}")
+    dd = dict(L=L, I=I, E=E, expert_format=0)
+    w = syn.expert_weights(dd, seed=1)
+    codes, scales = syn.mxfp8_random(syn.rng(1, 701), T, L)
+    ids = random_ids(np.random.default_rng(5), T, K, E, hot=3)
+    d = moe.dims(T, T)
+    d.experts = E
+    sample = np.sort(np.random.default_rng(6).choice(T * K, 40, replace=False)).astype(np.int32)
+    check_mx(orc, d, w, codes, scales, ids, sample)
+
+
+def test_ffn_bf16_toy(orc):
+    d0 = dict(syn.TOY)
+    T, K, E, L, I = d0["T"], d0["K"], d0["E"], d0["L"], d0["I"]
+    w = syn.expert_weights(d0, seed=0)
+    latent = syn.bf16_normal(syn.rng(0, 702), (T, L))
+    ids = random_ids(np.random.default_rng(7), T, K, E)
+    d = moe.dims_from(d0)
+    pairs, units, nu = build_lists(d, dev(ids))
+    rows = torch.zeros(T * K, L, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_ffn(d, dev(w["w13"]), None, dev(w["w2"]), None, dev(latent), None, pairs,
+                        units, nu, rows, None)
+    torch.cuda.synchronize()
+    allp = np.arange(T * K, dtype=np.int32)
+    ref = orc.ffn_bf16(allp, ids.reshape(-1), K, latent, w["w13"], w["w2"])
+    assert_close_bf16(host(rows), ref, "toy BF16 expert rows")

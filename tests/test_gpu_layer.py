@@ -1,0 +1,100 @@
+"""GPU parity of the whole layer (moe_layer) against the oracle.
+
+Toy latent MoE (T=8, BF16 experts): every output against the free-running oracle layer.
+Full layer (hidden 7168, latent 3584, 896 MXFP4 experts) at T=256 uniform and Zipf, and
+the sweep's T=65: every intermediate read from the documented workspace layout and
+checked teacher-forced -- each oracle step is fed the GPU's upstream outputs where a
+discrete decision follows (routing on the GPU's logits, quantisation on its latent, the
+experts on its codes and lists, Finalize on its rows): discrete results bit-exact,
+floating results within 2e-2 x RMS, Finalize exact; plus a free-running oracle layer on
+a few sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as syn
+import mixture_experts_decode_gemm_amd as moe
+from gpu_util import (assert_close, assert_close_bf16, bf16_ulp_dist, check_hidden, dev, f32,
+                      full_weights, host, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_layer(d, dw, x):
+    lw = moe.layer_weights(dw["w_gate"], dw["bias"], dw["w_down"], dw["w_shared_gu"],
+                           dw["w_shared_dn"], dw["norm_w"], dw["w_up"], dw["w13"], dw["s13"],
+                           dw["w2"], dw["s2"])
+    ws = torch.zeros(moe.moe_workspace_size(d), dtype=torch.uint8, device="cuda")
+    out = torch.empty(d.tokens, d.hidden, dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer(d, lw, dev(x), out, ws)
+    torch.cuda.synchronize()
+    return host(out), ws
+
+
+def test_toy_layer(orc):
+    d0 = dict(syn.TOY)
+    w = syn.layer_weights(d0, seed=0)
+    x = syn.layer_input(d0, seed=0)
+    dw = {k: (dev(v) if v is not None else None) for k, v in w.items()}
+    out, ws = run_layer(moe.dims_from(d0), dw, x)
+    ref, tr = orc.layer(d0, w, x, trace=True)
+    v = moe.workspace_views(moe.dims_from(d0), ws)
+    assert np.array_equal(host(v["ids"]), tr["ids"])
+    assert_close_bf16(out, ref, "toy layer out")
+
+
+@pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False)])
+def test_full_layer_teacher_forced(orc, T, zipf):
+    say(f"full layer T={T} zipf={zipf}: generating weights")
+    w, dw = full_weights(0, zipf)
+    d0 = syn.full_dims(T)
+    x = syn.layer_input(d0, seed=1)
+    d = moe.dims(T, 1020)
+    out, ws = run_layer(d, dw, x)
+    v = {k: host(t) for k, t in moe.workspace_views(d, ws).items()}
+    K, E = 16, 896
+    rng = np.random.default_rng(T)
+    toks = np.unique(np.r_[0, T - 1, rng.choice(T, 4, replace=False)])
+    # router logits (sampled tokens) and routing on the GPU's logits (all tokens)
+    assert_close(v["logits"][toks], orc.linear_f32(x[toks], w["w_gate"]), "logits")
+    rid, rw = orc.topk(v["logits"], w["bias"], K, 1, 2.5)
+    assert np.array_equal(v["ids"], rid)
+    assert np.array_equal(v["weights"].view(np.uint32), rw.view(np.uint32))
+    rl = orc.build_lists(v["ids"], E, 8)
+    assert np.array_equal(v["counts"], rl["counts"]) and np.array_equal(v["pairs"], rl["pairs"])
+    assert v["num_units"][0] == rl["num_units"]
+    assert np.array_equal(v["units_raw"][:rl["num_units"]], rl["units"])
+    D = int(np.count_nonzero(rl["counts"]))
+    say(f"  D={D} touched experts, {rl['num_units']} units")
+    # latent (sampled) and its MXFP8 codes (all tokens, on the GPU's latent)
+    assert_close_bf16(v["latent"][toks], orc.linear_bf16(x[toks], w["w_down"]), "latent")
+    rc, rs = orc.quant_mxfp8_bf16(v["latent"])
+    assert np.array_equal(v["codes"], rc) and np.array_equal(v["scales"], rs)
+    # experts on the GPU's codes, sampled pairs of the sampled tokens
+    pairs = np.array([t * K + k for t in toks for k in range(K)], np.int32)
+    pexp = v["ids"].reshape(-1)[pairs]
+    hc, hs, _ = orc.ffn_up_mx(pairs, pexp, K, v["codes"], v["scales"], w["w13"], w["s13"])
+    check_hidden(v["hidden"][pairs], v["hidden_scales"][pairs], hc, hs)
+    rows_tf = orc.ffn_down_mx(pexp, v["hidden"][pairs], v["hidden_scales"][pairs], w["w2"],
+                              w["s2"])
+    assert_close_bf16(v["rows"][pairs], rows_tf, "expert rows (oracle fed GPU hidden)")
+    rows_ref = orc.ffn_down_mx(pexp, hc, hs, w["w2"], w["s2"])
+    assert_close(f32(v["rows"][pairs]), f32(rows_ref), "expert rows (free-running, sanity)",
+                 tol=0.1)
+    # Finalize on the GPU's rows (all tokens): bit-exact
+    fin = orc.finalize(v["rows"], v["weights"])
+    assert np.array_equal(v["routed"], fin)
+    # RMSNorm on the GPU's routed latent, shared expert and output (sampled tokens)
+    nrm = orc.rmsnorm(v["routed"], w["norm_w"], 1e-5)
+    assert_close_bf16(v["normed"], nrm, "normed")
+    assert bf16_ulp_dist(v["normed"], nrm).max() <= 2
+    gu = orc.linear_bf16(x[toks], w["w_shared_gu"])
+    sh = orc.linear_bf16(orc.silu_mul_bf16(gu), w["w_shared_dn"])
+    assert_close_bf16(v["shared"][toks], sh, "shared expert")
+    o = orc.linear_add_bf16(v["normed"][toks], w["w_up"], v["shared"][toks])
+    assert_close_bf16(out[toks], o, "out (teacher-forced)")
+    # free-running oracle layer on two tokens (hidden code flips propagate: sanity bound)
+    sub = toks[:2]
+    d1 = dict(d0, T=len(sub))
+    ref = orc.layer(d1, w, x[sub])
+    assert_close(f32(out[sub]), f32(ref), "out (free-running oracle, sanity)", tol=0.1)

@@ -1,0 +1,134 @@
+"""GPU parity of the routing front: router GEMM logits (tolerance, sampled rows of the
+1020-token workload), sigmoid top-16 fed identical FP32 logits (ids and weights
+bit-exact), routing lists and unit windows (bit-exact, every field), with uniform and
+Zipf-skewed bias, small ragged shapes, and dropped ids."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as syn
+import mixture_experts_decode_gemm_amd as moe
+from gpu_util import assert_close, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_topk(d, logits, bias):
+    T, K = d.tokens, d.top_k
+    ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(d, None, None, dev(bias), dev(logits), ids, w, flags=moe.MOE_LOGITS_GIVEN)
+    torch.cuda.synchronize()
+    return host(ids), host(w)
+
+
+def run_lists(d, ids):
+    T, K, E = d.tokens, d.top_k, d.experts
+    P = T * K
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pairs = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+    nu_max = -(-P // d.unit_tokens) + E
+    units = torch.full((nu_max, 4), -7, dtype=torch.int32, device="cuda")
+    num_units = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_lists_workspace_size(d), dtype=torch.uint8, device="cuda")
+    moe.moe_build_lists(d, dev(ids), counts, offsets, pairs, units, num_units, ws)
+    torch.cuda.synchronize()
+    n = int(host(offsets)[E])
+    nu = host(num_units)
+    return dict(counts=host(counts), offsets=host(offsets), pairs=host(pairs)[:n],
+                units=host(units)[:nu[0]], num_units=int(nu[0]), dropped=int(nu[1]))
+
+
+def check_lists(orc, d, ids):
+    got = run_lists(d, ids)
+    ref = orc.build_lists(ids, d.experts, d.unit_tokens)
+    for k in ("counts", "offsets", "pairs", "units", "num_units", "dropped"):
+        assert np.array_equal(np.asarray(got[k]), np.asarray(ref[k])), k
+    return got
+
+
+@pytest.mark.parametrize("zipf", [False, True])
+def test_router_front_1020(orc, zipf):
+    T, E, H, K = 1020, 896, 7168, 16
+    say(f"router front T={T} zipf={zipf}")
+    x = syn.router_input(T, H, seed=0)
+    wg = syn.bf16_normal(syn.rng(0, 1), (E, H), 1 / np.sqrt(H))
+    bias = syn.routing_bias(E, 1 if zipf else 0, zipf)
+    d = moe.dims(T, T)
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_router_workspace_size(d), dtype=torch.uint8, device="cuda")
+    moe.moe_router_topk(d, dev(x), dev(wg), dev(bias), logits, ids, w, workspace=ws)
+    torch.cuda.synchronize()
+    lg = host(logits)
+    sample = np.r_[0:4, 500:504, T - 4:T]
+    ref_l = orc.linear_f32(x[sample], wg)
+    assert_close(lg[sample], ref_l, "router logits (12 sampled rows)")
+    # top-k on identical FP32 logits: bit-exact ids and weights
+    rid, rw = orc.topk(lg, bias, K, 1, 2.5)
+    assert np.array_equal(host(ids), rid)
+    assert np.array_equal(host(w).view(np.uint32), rw.view(np.uint32))
+    got = check_lists(orc, d, host(ids))
+    D = int(np.count_nonzero(got["counts"]))
+    say(f"  touched experts D={D}, units={got['num_units']}, max count={got['counts'].max()}")
+
+
+@pytest.mark.parametrize("T,E,K,unit", [(8, 32, 4, 8), (37, 23, 6, 8), (130, 896, 16, 16),
+                                        (1, 5, 5, 8), (255, 1024, 16, 8)])
+def test_topk_and_lists_shapes(orc, T, E, K, unit):
+    g = np.random.default_rng(T * 1000 + E)
+    logits = (g.standard_normal((T, E)) * 2).astype(np.float32)
+    logits[0, : min(E, 6)] = 0.0  # exact ties -> lower id first
+    bias = (g.standard_normal(E) * 0.05).astype(np.float32)
+    d = moe.dims(T, T, experts=E, top_k=K, unit_tokens=unit)
+    ids, w = run_topk(d, logits, bias)
+    rid, rw = orc.topk(logits, bias, K, 1, 2.5)
+    assert np.array_equal(ids, rid)
+    assert np.array_equal(w.view(np.uint32), rw.view(np.uint32))
+    check_lists(orc, d, ids)
+
+
+def test_topk_saturated_logits(orc):
+    # logits far in both tails exercise the sigmoid's boundary rules
+    T, E, K = 4, 64, 16
+    g = np.random.default_rng(11)
+    logits = (g.standard_normal((T, E)) * 60).astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    d = moe.dims(T, T, experts=E, top_k=K)
+    for renorm in (0, 1):
+        d.renormalize = renorm
+        ids, w = run_topk(d, logits, bias)
+        rid, rw = orc.topk(logits, bias, K, renorm, 2.5)
+        assert np.array_equal(ids, rid) and np.array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
+def test_lists_drop_invalid_and_repeated_ids(orc):
+    T, K, E = 70, 4, 9
+    g = np.random.default_rng(12)
+    ids = g.integers(-2, E + 2, size=(T, K)).astype(np.int32)
+    d = moe.dims(T, T, experts=E, top_k=K)
+    got = check_lists(orc, d, ids)
+    assert got["dropped"] > 0
+
+
+def test_lists_hot_expert_many_units(orc):
+    T, K, E = 1020, 16, 896
+    ids = np.zeros((T, K), np.int32)
+    for t in range(T):
+        ids[t] = np.r_[0, 1 + (np.arange(15) + t) % (E - 1)]
+    d = moe.dims(T, T)
+    got = check_lists(orc, d, ids)
+    assert got["counts"][0] == T
+
+
+def test_lists_deterministic(orc):
+    T, K, E = 512, 16, 896
+    g = np.random.default_rng(13)
+    ids = np.stack([g.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    d = moe.dims(T, T)
+    a = run_lists(d, ids)
+    b = run_lists(d, ids)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k]))

@@ -68,9 +68,11 @@ typedef struct {
 
 /* One unit window: `count` (1..unit_tokens) consecutive entries pairs[begin ..] of one
    expert's routing list ([wide] module summary: "every touched expert streams once per
-   8 of its tokens"). */
+   8 of its tokens").  expert_total is the expert's whole list length on its first window
+   and 0 on its later windows (the grouped FFN streams an expert once for all of its
+   windows). */
 typedef struct {
-    int32_t expert, begin, count, pad;
+    int32_t expert, begin, count, expert_total;
 } moe_unit;
 
 /* Expert weights (device).  MXFP4: w13 [E, 2I, L/2] bytes (element 2j in the low
@@ -110,12 +112,13 @@ size_t moe_router_workspace_size(const moe_dims* d);
 
 /* Routing lists and unit windows ([wide] WideRoute: each (token, slot) pair appended to
    its expert's list as token*K + slot; module summary: unit windows of 8).  Built without
-   atomics, deterministically: counts[E]; offsets[E+1] (exclusive prefix sum); pairs
-   [T*K] by expert ascending, ascending pair id inside a list; units for experts
-   ascending, windows of unit_tokens along each list; num_units[0] = number of units,
-   num_units[1] = dropped pairs (id outside [0,E) or repeated within a token; such pairs
-   are in no list).  units must hold ceil(T*K/unit_tokens) + E entries.  workspace:
-   >= moe_lists_workspace_size(d) bytes. */
+   atomic list claims, deterministically: counts[E]; offsets[E+1] (exclusive prefix sum);
+   pairs [T*K] by expert ascending, ascending pair id inside a list; units: windows of
+   unit_tokens consecutive list entries -- first the first window of every touched
+   expert (experts ascending), then every later window (experts ascending, list order);
+   num_units[4] = (number of units, dropped pairs (id outside [0,E) or repeated within a
+   token; such pairs are in no list), touched experts D, 0).  units must hold
+   ceil(T*K/unit_tokens) + E entries.  workspace: >= moe_lists_workspace_size(d) bytes. */
 moe_status moe_build_lists(const moe_dims* d, const int32_t* ids, int32_t* counts,
                            int32_t* offsets, int32_t* pairs, moe_unit* units,
                            int32_t* num_units, void* workspace, size_t ws_bytes, void* stream);
@@ -135,7 +138,9 @@ moe_status moe_quant_mxfp8(int32_t rows, int32_t cols, const void* x, uint8_t* c
    token p/K (FP32 accumulation); act = silu(h[:I]) * h[I:] in FP32; act -> MXFP8 (the
    moe_quant_mxfp8 rule); y = act_q W2e^T (FP32) rounded to BF16 into rows[p] [T*K, L].
    BF16 format: act = BF16 latent [T, L] (act_scales NULL), h and act rounded to BF16.
-   Rows of pairs in no list are not written.  num_units is read on the device.
+   Rows of pairs in no list are not written.  units and num_units are moe_build_lists'
+   output, read on the device: each touched expert is streamed once, for all of its
+   windows (the first D units name the touched experts and their list lengths).
    workspace: >= moe_ffn_workspace_size(d) bytes; on return it holds the MXFP8 hidden of
    every listed pair: codes u8 [T*K, I] at offset 0 and E8M0 scales u8 [T*K, I/32] at
    offset round_up(T*K*I, 256), indexed by pair id. */
@@ -188,7 +193,7 @@ size_t moe_workspace_size(const moe_dims* d); /* bytes at d->max_tokens; 0 if d 
 
 /* Byte offsets inside the moe_layer workspace of: 0 logits f32 [T,E], 1 ids [T,K],
    2 weights f32 [T,K], 3 counts [E], 4 offsets [E+1], 5 pairs [T*K], 6 units,
-   7 num_units [2], 8 latent bf16 [T,L], 9 codes u8 [T,L], 10 scales u8 [T,L/32],
+   7 num_units [4], 8 latent bf16 [T,L], 9 codes u8 [T,L], 10 scales u8 [T,L/32],
    11 rows bf16 [T*K,L], 12 routed bf16 [T,L], 13 shared bf16 [T,H], 14 normed bf16 [T,L],
    15 hidden codes u8 [T*K,I] (MXFP8 hidden of the experts, by pair id), 16 hidden scales
    u8 [T*K,I/32], 17 scratch (shared-expert intermediates, GEMM split partials, list

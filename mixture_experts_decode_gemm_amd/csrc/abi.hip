@@ -3,7 +3,7 @@
 // Nothing here allocates, frees or synchronises.
 #include <string.h>
 
-#include "../../include/moedecode.h"
+#include "moedecode.h"
 #include "kernels.h"
 
 using namespace moe;

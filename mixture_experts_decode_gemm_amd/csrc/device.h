@@ -64,6 +64,16 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
     return sign | code;
 }
 
+// ---- workgroup barrier over LDS only ----------------------------------------------------
+// __syncthreads() fences global memory too, which makes every wavefront wait for all of
+// its outstanding global loads (s_waitcnt vmcnt(0)) -- fatal to a software pipeline that
+// keeps the next tile's loads in flight across the barrier.  This barrier orders LDS only.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---- wave helpers ---------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -60,93 +60,398 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, v8i b, v4f c, int sa, int sb)
 constexpr int UP_COLS = 32;     // intermediate columns per up item
 constexpr int DOWN_ROWS = 256;  // W2 rows per down item
 
-__global__ __launch_bounds__(256) void k_ffn_up_mx(
-    int K, int L, int I, int unit, const uint8_t* __restrict__ w13,
-    const uint8_t* __restrict__ s13, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const int32_t* __restrict__ pairs,
-    const int4* __restrict__ units, const int32_t* __restrict__ num_units,
-    uint8_t* __restrict__ hid, uint8_t* __restrict__ hid_scales) {
-    __shared__ float red[4][4][4][64];   // [wave][tile][i][lane]
-    __shared__ float hbuf[64][17];       // [row of the item][token]
+__device__ __forceinline__ v8i as_fp4_operand(uint4 a) {
+    v8i r;
+    r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
+// Reduce the four wavefronts' partial H tiles (K split across wavefronts, added in a
+// fixed order), then act = silu(gate) * up in FP32 and one MXFP8 block of 32 columns
+// per token, written by pair id.  `red` and `hbuf` are LDS; called by all 256 threads.
+// `pair` is the pair id of token n0 + (lane % 16) (valid where that token exists); it
+// is exchanged by lane shuffles, so the epilogue issues no global load (a load here
+// would have to wait behind every prefetch still in flight).
+__device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float (*red)[4][4][64],
+                                            float (*hbuf)[17], int total, int n0, int pair,
+                                            int j, int I, uint8_t* __restrict__ hid,
+                                            uint8_t* __restrict__ hid_scales) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][m][i][lane] = acc[m][i];
+    lds_barrier();
+    {
+        const int m = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = ((red[0][m][i][l] + red[1][m][i][l]) + red[2][m][i][l]) +
+                            red[3][m][i][l];
+            hbuf[m * 16 + 4 * (l >> 4) + i][l & 15] = v;
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int nn = h * 8 + (threadIdx.x >> 5);
+        const int c = threadIdx.x & 31;
+        const float gt = hbuf[c][nn];
+        const float up = hbuf[32 + c][nn];
+        const float a = gt / (1.0f + expf(-gt)) * up;
+        uint32_t mag = __float_as_uint(a) & 0x7FFFFFFFu;
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)mag, off, 64);
+            mag = mag > o ? mag : o;
+        }
+        const int X = mx_block_exponent(mag);
+        const uint32_t code = e4m3_rne_sat(ldexpf(a, -X));
+        const int p = __shfl(pair, nn, 64);
+        if (n0 + nn < total) {
+            hid[(size_t)p * I + j * UP_COLS + c] = (uint8_t)code;
+            if (c == 0) hid_scales[(size_t)p * (I / 32) + j] = (uint8_t)(X + 127);
+        }
+    }
+    lds_barrier();
+}
+
+// Up projection, latent L = 512 * SPW.  Item = (touched expert u < D, 32 columns j): the
+// expert's tile (gate rows 32j.., up rows I+32j.., 64 x L FP4, 114 KiB at L = 3584) is
+// streamed ONCE into registers -- wavefront w holds K steps SPW*w .. SPW*w+SPW-1 of the
+// four 16-row tiles -- and applied to all of the expert's tokens, 16 per MFMA column
+// tile.  One workgroup per CU runs a software pipeline: while item i is computed, the
+// weights (and then the first activations) of item i + gridDim are already in flight,
+// so every CU keeps about one tile of HBM reads outstanding.  The tile's E8M0 scales are
+// staged in LDS.
+template <int SPW>
+struct UpStage {
+    uint4 w[4][SPW];  // FP4 weight fragments
+    uint4 sc[2];      // this thread's share of the 64 x L/32 scale tile
+    v8i b[SPW];       // FP8 activation fragments of the current token group
+    int sb[SPW];      // their scale bytes
+    int4 un;          // (expert, list begin, window, list length)
+    int j, pair;
+};
+
+// Every load below is issued unconditionally (indices are clamped, unused lanes load a
+// valid address and discard it) so that the same number of loads is outstanding on every
+// path: the compiler can then wait for exactly the current item's data (s_waitcnt
+// vmcnt(N)) and leave the next item's loads in flight.
+template <int SPW>
+__device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int nt, int I,
+                                                 const uint8_t* __restrict__ w13,
+                                                 const uint8_t* __restrict__ s13,
+                                                 const int32_t* __restrict__ pairs,
+                                                 const int4* __restrict__ units) {
+    constexpr int L = SPW * 512, SROW = L / 32, CH = SROW / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int u = item / nt;
+    st.j = item - u * nt;
+    st.un = units[u];
+    const int e = st.un.x;
+    // the first token group's pair ids, issued before the weights so that the
+    // activation addresses can wait on them without waiting on the weights
+    st.pair = pairs[st.un.y + min(r16, st.un.w - 1)];
+    const size_t ebase = (size_t)e * 2 * I;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = min((int)threadIdx.x + 256 * q, 64 * CH - 1);
+        const int row = c / CH, ch = c - row * CH, m = row >> 4;
+        const size_t R = ebase + (m >> 1) * I + st.j * UP_COLS + (m & 1) * 16 + (row & 15);
+        st.sc[q] = *(const uint4*)(s13 + R * SROW + ch * 16);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const size_t R = ebase + (m >> 1) * I + st.j * UP_COLS + (m & 1) * 16 + r16;
+        const uint8_t* base = w13 + R * (L / 2) + (SPW * wave) * 64 + 16 * g;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) st.w[m][i] = *(const uint4*)(base + i * 64);
+    }
+}
+
+template <int SPW>
+__device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int n0, int K,
+                                              const uint8_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ scales) {
+    constexpr int L = SPW * 512, SROW = L / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    // a lane past the group's last token holds a copy of a valid token: MFMA output
+    // column n depends on B column n only, and such columns are never stored
+    const int t = st.pair / K;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int s = SPW * wave + i;
+        st.b[i] = load_fp8x32(codes + (size_t)t * L + s * 128, g);
+        st.sb[i] = scales[(size_t)t * SROW + 4 * s + g];
+    }
+}
+
+template <int SPW>
+__device__ __forceinline__ void up_group(UpStage<SPW>& st, int n0, int I,
+                                         const int32_t* __restrict__ pairs,
+                                         uint8_t* __restrict__ hid, uint8_t* __restrict__ hid_scales,
+                                         const uint8_t* wsc, float (*red)[4][4][64],
+                                         float (*hbuf)[17]) {
+    constexpr int L = SPW * 512, SROW = L / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    v4f acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int s = SPW * wave + i;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int sa = wsc[(m * 16 + r16) * SROW + 4 * s + g];
+            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), st.b[i], acc[m], sa, st.sb[i]);
+        }
+    }
+    up_epilogue(acc, red, hbuf, st.un.w, n0, st.pair, st.j, I, hid, hid_scales);
+}
+
+template <int SPW>
+__device__ __forceinline__ void up_compute(UpStage<SPW>& st, int K, int I,
+                                           const uint8_t* __restrict__ codes,
+                                           const uint8_t* __restrict__ scales,
+                                           const int32_t* __restrict__ pairs,
+                                           uint8_t* __restrict__ hid,
+                                           uint8_t* __restrict__ hid_scales, uint8_t* wsc,
+                                           float (*red)[4][4][64], float (*hbuf)[17]) {
+    constexpr int L = SPW * 512, SROW = L / 32, CH = SROW / 16;
+    const int r16 = threadIdx.x & 15;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q;
+        if (c < 64 * CH) *(uint4*)(wsc + c * 16) = st.sc[q];
+    }
+    lds_barrier();
+    up_group(st, 0, I, pairs, hid, hid_scales, wsc, red, hbuf);
+    for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later token groups of a hot expert
+        st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
+        up_issue_acts(st, n0, K, codes, scales);
+        up_group(st, n0, I, pairs, hid, hid_scales, wsc, red, hbuf);
+    }
+}
+
+template <int SPW>
+__global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
+    int K, int I, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const int32_t* __restrict__ pairs, const int4* __restrict__ units,
+    const int32_t* __restrict__ num_units, uint8_t* __restrict__ hid,
+    uint8_t* __restrict__ hid_scales) {
+    constexpr int L = SPW * 512, SROW = L / 32;
+    __shared__ float red[4][4][4][64];
+    __shared__ float hbuf[64][17];
+    __shared__ __attribute__((aligned(16))) uint8_t wsc[64 * SROW];
+    const int nt = I / UP_COLS;
+    const int items = num_units[2] * nt;  // touched experts x column tiles
+    const int G = gridDim.x;
+    int item = blockIdx.x;
+    if (item >= items) return;
+    UpStage<SPW> A, B;
+    up_issue_weights(A, item, nt, I, w13, s13, pairs, units);
+    up_issue_acts(A, 0, K, codes, scales);
+    for (;;) {
+        // the next item (or, past the end, this one again: a harmless repeat load)
+        int nxt = item + G;
+        up_issue_weights(B, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
+        up_compute(A, K, I, codes, scales, pairs, hid, hid_scales, wsc, red, hbuf);
+        if (nxt >= items) break;
+        up_issue_acts(B, 0, K, codes, scales);
+        item = nxt;
+        nxt = item + G;
+        up_issue_weights(A, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
+        up_compute(B, K, I, codes, scales, pairs, hid, hid_scales, wsc, red, hbuf);
+        if (nxt >= items) break;
+        up_issue_acts(A, 0, K, codes, scales);
+        item = nxt;
+    }
+}
+
+// Up projection for any L % 128 == 0: wavefronts take K steps round-robin, weights are
+// loaded per step (fewer bytes in flight than the fast path).
+__global__ __launch_bounds__(256) void k_ffn_up_generic(
+    int K, int L, int I, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const int32_t* __restrict__ pairs, const int4* __restrict__ units,
+    const int32_t* __restrict__ num_units, uint8_t* __restrict__ hid,
+    uint8_t* __restrict__ hid_scales) {
+    __shared__ float red[4][4][4][64];
+    __shared__ float hbuf[64][17];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int nt = I / UP_COLS;
-    const int items = num_units[0] * nt;
+    const int items = num_units[2] * nt;
     const int steps = L / 128;
     const size_t wrow = (size_t)L / 2, srow = (size_t)L / 32;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int u = item / nt, j = item - u * nt;
         const int4 un = units[u];
-        const int e = un.x, begin = un.y, count = un.z;
-        for (int n0 = 0; n0 < count; n0 += 16) {
-            // this lane's token (B column) and its latent row
+        if (un.w == 0) continue;
+        const int e = un.x, begin = un.y, total = un.w;
+        for (int n0 = 0; n0 < total; n0 += 16) {
             const int n = n0 + r16;
-            const bool tok = n < count;
-            const int t = tok ? pairs[begin + n] / K : 0;
-            const uint8_t* arow = codes + (size_t)t * L;
-            const uint8_t* asrow = scales + (size_t)t * srow;
+            const bool tok = n < total;
+            const int pair = tok ? pairs[begin + n] : 0;
+            const int t = pair / K;
             v4f acc[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
-            for (int s = wave; s < steps; s += 4) {
+            for (int st = wave; st < steps; st += 4) {
                 v8i b = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
                 int sb = 127;
                 if (tok) {
-                    b = load_fp8x32(arow + s * 128, g);
-                    sb = asrow[s * 4 + g];
+                    b = load_fp8x32(codes + (size_t)t * L + st * 128, g);
+                    sb = scales[(size_t)t * srow + st * 4 + g];
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int row = (m >> 1) * I + j * UP_COLS + (m & 1) * 16 + r16;
-                    const size_t R = (size_t)e * 2 * I + row;
-                    const v8i a = load_fp4x32(w13 + R * wrow + s * 64 + g * 16);
-                    const int sa = s13[R * srow + s * 4 + g];
+                    const size_t R = (size_t)e * 2 * I + (m >> 1) * I + j * UP_COLS +
+                                     (m & 1) * 16 + r16;
+                    const v8i a = load_fp4x32(w13 + R * wrow + st * 64 + g * 16);
+                    const int sa = s13[R * srow + st * 4 + g];
                     acc[m] = mfma_fp4_fp8(a, b, acc[m], sa, sb);
                 }
             }
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) red[wave][m][i][lane] = acc[m][i];
-            __syncthreads();
-            {
-                const int m = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = ((red[0][m][i][l] + red[1][m][i][l]) + red[2][m][i][l]) +
-                                    red[3][m][i][l];
-                    hbuf[m * 16 + 4 * (l >> 4) + i][l & 15] = v;
-                }
-            }
-            __syncthreads();
-            // silu(gate) * up, then one MXFP8 block of 32 columns per token
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int nn = h * 8 + (threadIdx.x >> 5);
-                const int c = threadIdx.x & 31;
-                const float gt = hbuf[c][nn];
-                const float up = hbuf[32 + c][nn];
-                const float a = gt / (1.0f + expf(-gt)) * up;
-                uint32_t mag = __float_as_uint(a) & 0x7FFFFFFFu;
-#pragma unroll
-                for (int off = 16; off > 0; off >>= 1) {
-                    const uint32_t o = (uint32_t)__shfl_xor((int)mag, off, 64);
-                    mag = mag > o ? mag : o;
-                }
-                const int X = mx_block_exponent(mag);
-                const uint32_t code = e4m3_rne_sat(ldexpf(a, -X));
-                if (n0 + nn < count) {
-                    const int p = pairs[begin + n0 + nn];
-                    hid[(size_t)p * I + j * UP_COLS + c] = (uint8_t)code;
-                    if (c == 0) hid_scales[(size_t)p * (I / 32) + j] = (uint8_t)(X + 127);
-                }
-            }
-            __syncthreads();
+            up_epilogue(acc, red, hbuf, total, n0, pair, j, I, hid, hid_scales);
         }
     }
 }
 
-__global__ __launch_bounds__(256) void k_ffn_down_mx(
+// Down projection, intermediate I = 128 * IS.  Item = (touched expert u < D, 64*MT rows
+// of W2): wavefront w streams MT 16-row tiles (all IS K steps, plus the rows' scale
+// words) ONCE and applies them to all of the expert's pairs, 16 per MFMA column tile;
+// BF16 rows out.  Same one-workgroup-per-CU pipeline as the up projection: the next
+// item's weights are in flight while the current one is computed.
+template <int IS, int MT>
+struct DownStage {
+    uint4 w[MT][IS];
+    uint32_t sw[MT][IS];
+    v8i b[IS];
+    int sb[IS];
+    int4 un;
+    int j, pair;
+};
+
+template <int IS, int MT>
+__device__ __forceinline__ void down_issue_weights(DownStage<IS, MT>& st, int item, int nt, int L,
+                                                   const uint8_t* __restrict__ w2,
+                                                   const uint8_t* __restrict__ s2,
+                                                   const int32_t* __restrict__ pairs,
+                                                   const int4* __restrict__ units) {
+    constexpr int I = IS * 128, WROW = I / 2, SROW = I / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int u = item / nt;
+    st.j = item - u * nt;
+    st.un = units[u];
+    st.pair = pairs[st.un.y + min(r16, st.un.w - 1)];
+    const size_t R0 = (size_t)st.un.x * L + st.j * (64 * MT) + wave * (16 * MT) + r16;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const size_t R = R0 + m * 16;
+#pragma unroll
+        for (int s = 0; s < IS; ++s) {
+            st.w[m][s] = *(const uint4*)(w2 + R * WROW + s * 64 + 16 * g);
+            st.sw[m][s] = *(const uint32_t*)(s2 + R * SROW + 4 * s);
+        }
+    }
+}
+
+// lanes past the group's last pair load a valid pair's hidden; their output columns are
+// never stored
+template <int IS, int MT>
+__device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st,
+                                                const uint8_t* __restrict__ hid,
+                                                const uint8_t* __restrict__ hid_scales) {
+    constexpr int I = IS * 128, SROW = I / 32;
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int s = 0; s < IS; ++s) {
+        st.b[s] = load_fp8x32(hid + (size_t)st.pair * I + s * 128, g);
+        st.sb[s] = hid_scales[(size_t)st.pair * SROW + 4 * s + g];
+    }
+}
+
+template <int IS, int MT>
+__device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L,
+                                           uint16_t* __restrict__ rows) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    v4f acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < IS; ++s)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][s]), st.b[s], acc[m],
+                                  (int)((st.sw[m][s] >> (8 * g)) & 0xFFu), st.sb[s]);
+    if (n0 + r16 < st.un.w) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int row = st.j * (64 * MT) + wave * (16 * MT) + m * 16 + 4 * g;
+            uint2 o;
+            o.x = pack_bf16x2(acc[m][0], acc[m][1]);
+            o.y = pack_bf16x2(acc[m][2], acc[m][3]);
+            *(uint2*)(rows + (size_t)st.pair * L + row) = o;
+        }
+    }
+}
+
+template <int IS, int MT>
+__device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L,
+                                             const uint8_t* __restrict__ hid,
+                                             const uint8_t* __restrict__ hid_scales,
+                                             const int32_t* __restrict__ pairs,
+                                             uint16_t* __restrict__ rows) {
+    const int r16 = threadIdx.x & 15;
+    down_group(st, 0, L, rows);
+    for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later pair groups of a hot expert
+        st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
+        down_issue_acts(st, hid, hid_scales);
+        down_group(st, n0, L, rows);
+    }
+}
+
+template <int IS, int MT>
+__global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
+    int L, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
+    const uint8_t* __restrict__ hid, const uint8_t* __restrict__ hid_scales,
+    const int32_t* __restrict__ pairs, const int4* __restrict__ units,
+    const int32_t* __restrict__ num_units, uint16_t* __restrict__ rows) {
+    const int nt = L / (64 * MT);
+    const int items = num_units[2] * nt;
+    const int G = gridDim.x;
+    int item = blockIdx.x;
+    if (item >= items) return;
+    DownStage<IS, MT> A, B;
+    down_issue_weights(A, item, nt, L, w2, s2, pairs, units);
+    down_issue_acts(A, hid, hid_scales);
+    for (;;) {
+        int nxt = item + G;
+        down_issue_weights(B, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
+        down_compute(A, L, hid, hid_scales, pairs, rows);
+        if (nxt >= items) break;
+        down_issue_acts(B, hid, hid_scales);
+        item = nxt;
+        nxt = item + G;
+        down_issue_weights(A, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
+        down_compute(B, L, hid, hid_scales, pairs, rows);
+        if (nxt >= items) break;
+        down_issue_acts(A, hid, hid_scales);
+        item = nxt;
+    }
+}
+
+// Down projection for any I % 128 == 0 (weights loaded per K step)
+__global__ __launch_bounds__(256) void k_ffn_down_generic(
     int L, int I, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
     const uint8_t* __restrict__ hid, const uint8_t* __restrict__ hid_scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
@@ -154,32 +459,33 @@ __global__ __launch_bounds__(256) void k_ffn_down_mx(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int nt = L / DOWN_ROWS;
-    const int items = num_units[0] * nt;
+    const int items = num_units[2] * nt;
     const int steps = I / 128;
     const size_t wrow = (size_t)I / 2, srow = (size_t)I / 32;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int u = item / nt, j = item - u * nt;
         const int4 un = units[u];
-        const int e = un.x, begin = un.y, count = un.z;
-        for (int n0 = 0; n0 < count; n0 += 16) {
+        if (un.w == 0) continue;
+        const int e = un.x, begin = un.y, total = un.w;
+        for (int n0 = 0; n0 < total; n0 += 16) {
             const int n = n0 + r16;
-            const bool tok = n < count;
+            const bool tok = n < total;
             const int p = tok ? pairs[begin + n] : 0;
             v4f acc[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < steps; ++s) {
+            for (int st = 0; st < steps; ++st) {
                 v8i b = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
                 int sb = 127;
                 if (tok) {
-                    b = load_fp8x32(hid + (size_t)p * I + s * 128, g);
-                    sb = hid_scales[(size_t)p * srow + s * 4 + g];
+                    b = load_fp8x32(hid + (size_t)p * I + st * 128, g);
+                    sb = hid_scales[(size_t)p * srow + st * 4 + g];
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const size_t R = (size_t)e * L + j * DOWN_ROWS + wave * 64 + m * 16 + r16;
-                    const v8i a = load_fp4x32(w2 + R * wrow + s * 64 + g * 16);
-                    const int sa = s2[R * srow + s * 4 + g];
+                    const v8i a = load_fp4x32(w2 + R * wrow + st * 64 + g * 16);
+                    const int sa = s2[R * srow + st * 4 + g];
                     acc[m] = mfma_fp4_fp8(a, b, acc[m], sa, sb);
                 }
             }
@@ -197,15 +503,23 @@ __global__ __launch_bounds__(256) void k_ffn_down_mx(
     }
 }
 
-static int persistent_blocks(int max_items) {
+// compute units of the current device (queried once; 256 on MI355X)
+static int num_cus() {
     static int cus = 0;
     if (!cus) {
-        int dev = 0;
-        hipGetDevice(&dev);
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (cus <= 0) cus = 256;
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+        else
+            cus = 256;
     }
-    const int cap = cus * 8;
+    return cus;
+}
+
+static int persistent_blocks(int max_items, int per_cu) {
+    const int cap = num_cus() * per_cu;
     return max_items < cap ? (max_items > 0 ? max_items : 1) : cap;
 }
 
@@ -214,14 +528,40 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
                          const int32_t* units, const int32_t* num_units, void* rows,
                          uint8_t* hid, uint8_t* hsc, hipStream_t s) {
-    const int P = T * K;
-    const int max_units = (P + unit - 1) / unit + E;
-    hipLaunchKernelGGL(k_ffn_up_mx, dim3(persistent_blocks(max_units * (I / UP_COLS))), dim3(256),
-                       0, s, K, L, I, unit, w13, s13, codes, scales, pairs, (const int4*)units,
-                       num_units, hid, hsc);
-    hipLaunchKernelGGL(k_ffn_down_mx, dim3(persistent_blocks(max_units * (L / DOWN_ROWS))),
-                       dim3(256), 0, s, L, I, w2, s2, hid, hsc, pairs, (const int4*)units,
-                       num_units, (uint16_t*)rows);
+    (void)T;
+    (void)unit;
+    const int4* un = (const int4*)units;
+    const int up_items = E * (I / UP_COLS);  // an upper bound: the kernels read D on the device
+    const int cus = num_cus();
+    const dim3 blk(256);
+    switch (L % 512 == 0 ? L / 512 : 0) {
+#define MOE_UP(SPW)                                                                          \
+    case SPW:                                                                                \
+        hipLaunchKernelGGL(k_ffn_up_fast<SPW>, dim3(up_items < cus ? up_items : cus), blk, 0, \
+                           s, K, I, w13, s13, codes, scales, pairs, un, num_units, hid, hsc);  \
+        break;
+        MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7)
+#undef MOE_UP
+        default:
+            hipLaunchKernelGGL(k_ffn_up_generic, dim3(persistent_blocks(up_items, 8)), blk, 0, s,
+                               K, L, I, w13, s13, codes, scales, pairs, un, num_units, hid, hsc);
+    }
+    const int MTsel = L % 512 == 0 ? 8 : (L % 256 == 0 ? 4 : 0);
+    const int down_items = MTsel ? E * (L / (64 * MTsel)) : E * (L / DOWN_ROWS);
+    const int dgrid = down_items < cus ? down_items : cus;
+    switch (MTsel * 10 + I / 128) {
+#define MOE_DOWN(MT, IS)                                                                     \
+    case MT * 10 + IS:                                                                       \
+        hipLaunchKernelGGL((k_ffn_down_fast<IS, MT>), dim3(dgrid), blk, 0, s, L, w2, s2, hid,  \
+                           hsc, pairs, un, num_units, (uint16_t*)rows);                      \
+        break;
+        MOE_DOWN(8, 1) MOE_DOWN(8, 2) MOE_DOWN(8, 4) MOE_DOWN(4, 1) MOE_DOWN(4, 2)
+        MOE_DOWN(4, 4)
+#undef MOE_DOWN
+        default:
+            hipLaunchKernelGGL(k_ffn_down_generic, dim3(persistent_blocks(down_items, 8)), blk, 0,
+                               s, L, I, w2, s2, hid, hsc, pairs, un, num_units, (uint16_t*)rows);
+    }
     return hipGetLastError();
 }
 
@@ -272,7 +612,7 @@ hipError_t launch_ffn_bf16(int T, int K, int E, int L, int I, int unit, const vo
                            const int32_t* units, const int32_t* num_units, void* rows,
                            hipStream_t s) {
     const int max_units = (T * K + unit - 1) / unit + E;
-    hipLaunchKernelGGL(k_ffn_bf16, dim3(persistent_blocks(max_units)), dim3(256),
+    hipLaunchKernelGGL(k_ffn_bf16, dim3(persistent_blocks(max_units, 8)), dim3(256),
                        (size_t)3 * I * sizeof(float), s, K, L, I, (const uint16_t*)w13,
                        (const uint16_t*)w2, (const uint16_t*)latent, pairs, (const int4*)units,
                        num_units, (uint16_t*)rows);

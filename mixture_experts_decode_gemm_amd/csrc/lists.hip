@@ -8,10 +8,11 @@
 //            tokens that chose expert e (LDS bit-ORs, whose result is order-free; an id
 //            outside [0,E) sets nothing, a repeated id sets the same bit once);
 //   scan  -- one workgroup, one thread per expert: counts, per-word running offsets,
-//            exclusive prefix sums over experts (offsets, unit bases), the units;
+//            exclusive prefix sums over experts (offsets, window indices), the units
+//            (the first window of every touched expert first, then the later windows);
 //   fill  -- one thread per (word, expert): the set bits in ascending token order give
 //            the list entries; the slot k is the first slot of that token holding e.
-// Lists therefore hold ascending pair ids, and units run over experts ascending.
+// Lists therefore hold ascending pair ids.
 #include "device.h"
 #include "kernels.h"
 
@@ -82,23 +83,28 @@ __global__ __launch_bounds__(1024) void k_lists_scan(int T, int K, int E, int un
             wordoff[(size_t)w * E + e] = c;
             c += __popc(bm[(size_t)w * E + e]);
         }
-    int total_pairs, total_units;
+    int total_pairs, touched, later_total;
     const int off = block_exclusive_scan_1024(c, smem, &total_pairs);
     const int nu = (c + unit - 1) / unit;
-    const int ub = block_exclusive_scan_1024(nu, smem, &total_units);
+    // the first window of every touched expert, then every later window
+    const int fi = block_exclusive_scan_1024(c > 0 ? 1 : 0, smem, &touched);
+    const int li = block_exclusive_scan_1024(nu > 1 ? nu - 1 : 0, smem, &later_total);
     if (e < E) {
         counts[e] = c;
         offsets[e] = off;
         for (int w = 0; w < W; ++w) wordoff[(size_t)w * E + e] += off;
-        for (int j = 0; j < nu; ++j) {
+        if (c > 0) units[fi] = make_int4(e, off, c < unit ? c : unit, c);
+        for (int j = 1; j < nu; ++j) {
             const int rest = c - j * unit;
-            units[ub + j] = make_int4(e, off + j * unit, rest < unit ? rest : unit, 0);
+            units[touched + li + j - 1] = make_int4(e, off + j * unit, rest < unit ? rest : unit, 0);
         }
     }
     if (threadIdx.x == 0) {
         offsets[E] = total_pairs;
-        num_units[0] = total_units;
+        num_units[0] = touched + later_total;
         num_units[1] = T * K - total_pairs;
+        num_units[2] = touched;
+        num_units[3] = 0;
     }
 }
 

@@ -184,12 +184,13 @@ def build_lists(ids, E, unit_tokens=8):
     offsets = np.empty(E + 1, np.int32)
     pairs = np.full(max(P, 1), -1, np.int32)
     units = np.zeros((P + E + 1, 4), np.int32)
-    nu = np.zeros(2, np.int32)
+    nu = np.zeros(4, np.int32)
     lib().orc_build_lists(T, K, E, unit_tokens, _p(ids), _p(counts), _p(offsets), _p(pairs),
                           _p(units), _p(nu))
     n = int(offsets[E])
     return dict(counts=counts, offsets=offsets, pairs=pairs[:n].copy(),
-                units=units[: int(nu[0])].copy(), num_units=int(nu[0]), dropped=int(nu[1]))
+                units=units[: int(nu[0])].copy(), num_units=int(nu[0]), dropped=int(nu[1]),
+                touched=int(nu[2]))
 
 
 def quant_mxfp8_bf16(x):

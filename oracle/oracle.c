@@ -229,8 +229,12 @@ void orc_topk(int T, int E, int K, const float* logits, const float* bias, int r
    token*16 + slot) and the module summary ("unit windows built from the routing
    lists: every touched expert streams once per 8 of its tokens").  The pages fill
    lists with atomic claims, so the order inside a list is theirs to choose; here a
-   list holds its pairs in ascending pair id.  Units run over experts ascending and,
-   inside an expert, over windows of unit_tokens consecutive list entries.
+   list holds its pairs in ascending pair id.  A unit is a window of unit_tokens
+   consecutive entries of one list: (expert, first list entry, window length, the
+   expert's list length on its first window and 0 on later ones).  The units list the
+   first window of every touched expert (experts ascending), then every later window
+   (experts ascending, windows in list order).  num_units = (units, dropped pairs,
+   touched experts, 0).
    A pair whose id lies outside [0,E), or whose expert already appeared at an earlier
    slot of the same token, is dropped and counted. */
 int orc_build_lists(int T, int K, int E, int unit_tokens, const int32_t* ids, int32_t* counts,
@@ -258,9 +262,20 @@ int orc_build_lists(int T, int K, int E, int unit_tokens, const int32_t* ids, in
     for (int e = 0; e < E; ++e)
         for (int p = 0; p < P; ++p)
             if (listed[p] && ids[p] == e) pairs[n++] = p;
-    int u = 0;
+    /* the first window of every touched expert, experts ascending, then every later
+       window, experts ascending and windows in list order */
+    int u = 0, touched = 0;
     for (int e = 0; e < E; ++e)
-        for (int j = 0; j * unit_tokens < counts[e]; ++j) {
+        if (counts[e] > 0) {
+            units[4 * u + 0] = e;
+            units[4 * u + 1] = offsets[e];
+            units[4 * u + 2] = counts[e] < unit_tokens ? counts[e] : unit_tokens;
+            units[4 * u + 3] = counts[e];
+            ++u;
+            ++touched;
+        }
+    for (int e = 0; e < E; ++e)
+        for (int j = 1; j * unit_tokens < counts[e]; ++j) {
             int rest = counts[e] - j * unit_tokens;
             units[4 * u + 0] = e;
             units[4 * u + 1] = offsets[e] + j * unit_tokens;
@@ -270,6 +285,8 @@ int orc_build_lists(int T, int K, int E, int unit_tokens, const int32_t* ids, in
         }
     num_units[0] = u;
     num_units[1] = dropped;
+    num_units[2] = touched;
+    num_units[3] = 0;
     free(listed);
     return dropped;
 }
@@ -528,7 +545,7 @@ void orc_layer(const orc_dims* d, const orc_weights* w, const uint16_t* x, uint1
     int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
     int32_t* pairs = (int32_t*)malloc(sizeof(int32_t) * (P > 0 ? P : 1));
     int32_t* units = (int32_t*)malloc(sizeof(int32_t) * 4 * (P + (size_t)E + 1));
-    int32_t nu[2];
+    int32_t nu[4];
     int32_t* pexp = (int32_t*)malloc(sizeof(int32_t) * (P > 0 ? P : 1));
     uint16_t* latent = (uint16_t*)malloc(2 * (size_t)T * L);
     uint8_t* codes = (uint8_t*)malloc((size_t)T * L);

@@ -38,7 +38,10 @@ void  orc_sigmoid_constants(float out[11]); /* log2e, ln2_hi, ln2_lo, c0..c7 */
 void orc_linear_f32(int M, int N, int K, const uint16_t* x, const uint16_t* w, float* out);
 void orc_topk(int T, int E, int K, const float* logits, const float* bias, int renormalize,
               float scale, int32_t* ids, float* weights);
-/* returns the number of dropped pairs (expert id outside [0,E) or repeated in a token) */
+/* returns the number of dropped pairs (expert id outside [0,E) or repeated in a token);
+   units [n,4] = (expert, first list entry, window length, list length on the first
+   window of an expert else 0), first windows first; num_units[4] = (units, dropped,
+   touched experts, 0) */
 int  orc_build_lists(int T, int K, int E, int unit_tokens, const int32_t* ids, int32_t* counts,
                      int32_t* offsets, int32_t* pairs, int32_t* units, int32_t* num_units);
 

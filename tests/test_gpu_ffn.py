@@ -10,7 +10,8 @@ import torch
 
 import moe_synth as syn
 import mixture_experts_decode_gemm_amd as moe
-from gpu_util import assert_close, assert_close_bf16, check_hidden, dev, f32, host, say
+from gpu_util import (assert_close, assert_close_bf16, check_hidden, dev, f32,
+                      hidden_error_bound, host, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +58,8 @@ def check_mx(orc, d, w, codes, scales, ids, sample):
     rows, hid, hsc = run_ffn_mx(d, w, codes, scales, ids)
     pexp = ids.reshape(-1)[sample]
     hc, hs, hf = orc.ffn_up_mx(sample, pexp, K, codes, scales, w["w13"], w["s13"])
-    check_hidden(hid[sample], hsc[sample], hc, hs)
+    delta = hidden_error_bound(codes, scales, w["w13"], w["s13"], sample, pexp, K, I)
+    check_hidden(hid[sample], hsc[sample], hc, hs, hf, delta)
     # second half teacher-forced on the GPU's hidden codes
     ref_tf = orc.ffn_down_mx(pexp, hid[sample], hsc[sample], w["w2"], w["s2"])
     assert_close_bf16(rows[sample], ref_tf, "rows (oracle fed GPU hidden)")

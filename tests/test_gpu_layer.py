@@ -15,7 +15,7 @@ import torch
 import moe_synth as syn
 import mixture_experts_decode_gemm_amd as moe
 from gpu_util import (assert_close, assert_close_bf16, bf16_ulp_dist, check_hidden, dev, f32,
-                      full_weights, host, say)
+                      full_weights, hidden_error_bound, host, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,8 +73,9 @@ def test_full_layer_teacher_forced(orc, T, zipf):
     # experts on the GPU's codes, sampled pairs of the sampled tokens
     pairs = np.array([t * K + k for t in toks for k in range(K)], np.int32)
     pexp = v["ids"].reshape(-1)[pairs]
-    hc, hs, _ = orc.ffn_up_mx(pairs, pexp, K, v["codes"], v["scales"], w["w13"], w["s13"])
-    check_hidden(v["hidden"][pairs], v["hidden_scales"][pairs], hc, hs)
+    hc, hs, hf = orc.ffn_up_mx(pairs, pexp, K, v["codes"], v["scales"], w["w13"], w["s13"])
+    delta = hidden_error_bound(v["codes"], v["scales"], w["w13"], w["s13"], pairs, pexp, K, 512)
+    check_hidden(v["hidden"][pairs], v["hidden_scales"][pairs], hc, hs, hf, delta)
     rows_tf = orc.ffn_down_mx(pexp, v["hidden"][pairs], v["hidden_scales"][pairs], w["w2"],
                               w["s2"])
     assert_close_bf16(v["rows"][pairs], rows_tf, "expert rows (oracle fed GPU hidden)")

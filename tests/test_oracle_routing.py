@@ -165,13 +165,12 @@ def brute_lists(ids, E, unit):
                 dropped += 1
     listed.sort()
     counts = np.array([sum(1 for e, _ in listed if e == x) for x in range(E)], np.int32)
-    units = []
-    off = 0
-    for e in range(E):
-        for j in range(0, counts[e], unit):
-            units.append((e, off + j, min(unit, counts[e] - j), 0))
-        off += counts[e]
-    return counts, np.array([p for _, p in listed], np.int32), np.array(units, np.int32).reshape(-1, 4), dropped
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    first = [(e, offs[e], min(unit, counts[e]), counts[e]) for e in range(E) if counts[e] > 0]
+    later = [(e, offs[e] + j, min(unit, counts[e] - j), 0)
+             for e in range(E) for j in range(unit, counts[e], unit)]
+    units = np.array(first + later, np.int32).reshape(-1, 4)
+    return counts, np.array([p for _, p in listed], np.int32), units, dropped
 
 
 def test_lists_vs_brute_force_and_invariants(orc):
@@ -190,7 +189,16 @@ def test_lists_vs_brute_force_and_invariants(orc):
         seg = r["pairs"][r["offsets"][e]:r["offsets"][e + 1]]
         assert np.all(np.diff(seg) > 0) and np.all(ids.reshape(-1)[seg] == e)
     assert r["num_units"] == sum(-(-int(x) // 8) for x in r["counts"])
+    assert r["touched"] == int(np.count_nonzero(r["counts"]))
     assert np.all(r["units"][:, 2] <= 8) and np.all(r["units"][:, 2] >= 1)
+    # the windows of each expert tile its list exactly
+    for e in range(E):
+        win = sorted((b, c) for x, b, c, _ in r["units"] if x == e)
+        pos = r["offsets"][e]
+        for b, c in win:
+            assert b == pos
+            pos += c
+        assert pos == r["offsets"][e + 1]
 
 
 def test_lists_drop_invalid_and_repeated(orc):
@@ -199,7 +207,7 @@ def test_lists_drop_invalid_and_repeated(orc):
     assert r["dropped"] == 4
     assert r["counts"].tolist() == [2, 1, 1]
     assert r["pairs"].tolist() == [0, 6, 1, 5]
-    assert r["units"].tolist() == [[0, 0, 2, 0], [1, 2, 1, 0], [2, 3, 1, 0]]
+    assert r["units"].tolist() == [[0, 0, 2, 2], [1, 2, 1, 1], [2, 3, 1, 1]]
 
 
 def test_lists_unit_windows_hot_expert(orc):
@@ -207,5 +215,8 @@ def test_lists_unit_windows_hot_expert(orc):
     ids = np.stack([np.zeros(T, np.int32), 1 + (np.arange(T, dtype=np.int32) % 3)], axis=1)
     r = orc.build_lists(ids, E, 8)
     assert r["counts"].tolist() == [50, 17, 17, 16]
-    assert r["num_units"] == 7 + 3 + 3 + 2
-    assert r["units"][6].tolist() == [0, 48, 2, 0]
+    assert r["num_units"] == 7 + 3 + 3 + 2 and r["touched"] == 4
+    assert r["units"][:4].tolist() == [[0, 0, 8, 50], [1, 50, 8, 17], [2, 67, 8, 17],
+                                       [3, 84, 8, 16]]
+    assert r["units"][4].tolist() == [0, 8, 8, 0] and r["units"][9].tolist() == [0, 48, 2, 0]
+    assert r["units"][10].tolist() == [1, 58, 8, 0] and r["units"][14].tolist() == [3, 92, 8, 0]

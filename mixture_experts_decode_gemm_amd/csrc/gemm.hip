@@ -3,27 +3,49 @@
 // ep/layer page, stock_order and the "cuBLAS addmm: one rounding" of the up-projection).
 //
 // Decode shapes are skinny (M = tokens, 65..1020) and wide (N up to 12288, K up to 7168):
-// the weights are streamed once, the activations re-read from L2.  Tiles are 128 x 128
-// with BK = 64, 256 threads as 2 x 2 wavefronts of 64 x 64 (4 x 4 MFMA 16x16x32 BF16
-// tiles), LDS single-buffered with the next K-step prefetched into registers.  When the
-// tile grid is too small to fill the 256 CUs the K range is split; the split partials go
-// to an FP32 scratch and a second kernel adds them in split order and applies the
-// epilogue (FP32 out, BF16 out, or BF16 out of FP32(add) + acc).
+// the weights must stream from HBM at full rate, which takes many bytes in flight per CU.
+// Tiles are 128 x 64 with BK = 64; both operand tiles go global -> LDS by direct loads
+// (no register staging), rows XOR-swizzled in 16-byte chunks so that the MFMA fragment
+// reads of 16 rows hit distinct LDS bank groups; NS LDS stages with NS - 1 K-steps in
+// flight.  Small stages (24 KB each) let three workgroups share a CU, and it is that
+// occupancy, more than pipeline depth, which keeps HBM busy.  Four wavefronts as 2 x 2,
+// each 64 x 32 (4 x 2 MFMA 16x16x32 BF16 tiles); FP32 accumulation.  When the tile grid
+// is too small to fill the CUs the K range is split; split partials go to an FP32 scratch
+// and a second kernel adds them in split order and applies the epilogue (FP32 out, BF16
+// out, or BF16 out of FP32(add) + acc).
 #include "device.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDSK = BK + 8;  // +8: rows 144 B apart
+constexpr int GEMM_BM = 128, GEMM_BN = 64, BK = 64;
+constexpr int GEMM_NS = 2;                                    // LDS stages
+constexpr int GEMM_LDS = GEMM_NS * (GEMM_BM + GEMM_BN) * BK * 2;  // bytes per workgroup
+constexpr int GEMM_WG_PER_CU = (160 * 1024 / GEMM_LDS) < 4 ? (160 * 1024 / GEMM_LDS) : 4;
 
 struct Split {
     int S, kchunk;
 };
 
+static int gemm_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
 static Split choose_split(int M, int N, int K) {
-    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    int S = (512 + tiles - 1) / tiles;
-    const int maxS = K / 256 > 0 ? K / 256 : 1;
+    const int tiles = ((M + GEMM_BM - 1) / GEMM_BM) * ((N + GEMM_BN - 1) / GEMM_BN);
+    const int target = gemm_cus() * GEMM_WG_PER_CU;  // one round of resident workgroups
+    int S = (target + tiles - 1) / tiles;
+    const int maxS = K / 512 > 0 ? K / 512 : 1;  // keep at least 8 K-steps per split
     if (S > maxS) S = maxS;
     if (S < 1) S = 1;
     int kchunk = ((K / S + BK - 1) / BK) * BK;
@@ -34,8 +56,8 @@ static Split choose_split(int M, int N, int K) {
 size_t gemm_scratch_bytes(int M, int N, int K) {
     // the largest split partial buffer over every token count up to M
     size_t best = 0;
-    for (int mt = 1; mt <= (M + BM - 1) / BM; ++mt) {
-        const int m = mt * BM < M ? mt * BM : M;
+    for (int mt = 1; mt <= (M + GEMM_BM - 1) / GEMM_BM; ++mt) {
+        const int m = mt * GEMM_BM < M ? mt * GEMM_BM : M;
         const Split sp = choose_split(m, N, K);
         if (sp.S > 1) {
             const size_t b = (size_t)sp.S * m * N * sizeof(float);
@@ -57,78 +79,109 @@ __device__ __forceinline__ void store_out(void* out, const void* add, size_t idx
     }
 }
 
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 // MODE: 0 FP32 out, 1 BF16 out, 2 BF16 out + add; 3 FP32 split partial (out = scratch)
-template <int MODE>
+template <int MODE, int NS>
 __global__ __launch_bounds__(256) void k_gemm(int M, int N, int K, int kchunk,
                                               const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ w, void* out,
                                               const void* add) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDSK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDSK];
+    constexpr int BM = GEMM_BM, BN = GEMM_BN;
+    constexpr int LA = BM * 8 / 256, LB = BN * 8 / 256;  // 16-byte chunks per thread per step
+    // stage s: [BM rows of x][BN rows of w], 128 bytes a row; row r's chunk c at c ^ ((r>>1)&7)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][(BM + BN) * BK * 2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
     const int kb = blockIdx.z * kchunk;
     const int ke = min(K, kb + kchunk);
+    const int nsteps = (ke - kb) / BK;
 
-    uint4 ra[4], rb[4];
-    auto gload = [&](int k0) {
+    // the direct loads of a wavefront fill 64 consecutive 16-byte LDS chunks, so LDS chunk
+    // p = i*256 + tid receives the global chunk that belongs there after the swizzle.
+    // Rows past M or N read a valid row (clamped); their results are never stored.
+    const uint16_t* srcA[LA];
+    const uint16_t* srcB[LB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + 256 * i;
-            const int r = q >> 3, c = (q & 7) * 8;
-            ra[i] = (m0 + r < M) ? *(const uint4*)(x + (size_t)(m0 + r) * K + k0 + c)
-                                 : make_uint4(0, 0, 0, 0);
-            rb[i] = (n0 + r < N) ? *(const uint4*)(w + (size_t)(n0 + r) * K + k0 + c)
-                                 : make_uint4(0, 0, 0, 0);
-        }
+    for (int i = 0; i < LA; ++i) {
+        const int p = i * 256 + tid, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+        srcA[i] = x + (size_t)min(m0 + r, M - 1) * K + 8 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int p = i * 256 + tid, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+        srcB[i] = w + (size_t)min(n0 + r, N - 1) * K + 8 * c;
+    }
+    auto issue = [&](int slot, int k0) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + k0),
+                                             (lds_ptr)(lds[slot] + (i * 256 + wave * 64) * 16),
+                                             16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < LB; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(srcB[i] + k0),
+                (lds_ptr)(lds[slot] + BM * BK * 2 + (i * 256 + wave * 64) * 16), 16, 0, 0);
     };
-    v4f acc[4][4];
+    v4f acc[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 2; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    gload(kb);
-    for (int k0 = kb; k0 < ke; k0 += BK) {
-        __syncthreads();
+    // prologue: NS - 1 steps in flight (past the end: a repeat of the first step, unused,
+    // so that every thread always has the same number of loads outstanding)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + 256 * i;
-            const int r = q >> 3, c = (q & 7) * 8;
-            *(uint4*)(As + r * LDSK + c) = ra[i];
-            *(uint4*)(Bs + r * LDSK + c) = rb[i];
-        }
-        __syncthreads();
-        if (k0 + BK < ke) gload(k0 + BK);
+    for (int st = 0; st < NS - 1; ++st) issue(st, st < nsteps ? kb + st * BK : kb);
+    for (int ks = 0; ks < nsteps; ++ks) {
+        wait_vmcnt<(NS - 2) * (LA + LB)>();  // this thread's loads of step ks have landed
+        lds_barrier();                       // ... everyone's; step ks - 1 fully consumed
+        const int nk = ks + NS - 1;
+        issue(nk % NS, nk < nsteps ? kb + nk * BK : kb);
+        const uint8_t* At = lds[ks % NS];
+        const uint8_t* Bt = At + BM * BK * 2;
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 fa[4], fb[4];
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = kk * 4 + g;
+            bf16x8 fb[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                fa[i] = *(const bf16x8*)(As + (wm * 64 + i * 16 + (lane & 15)) * LDSK + kk +
-                                         8 * (lane >> 4));
-                fb[i] = *(const bf16x8*)(Bs + (wn * 64 + i * 16 + (lane & 15)) * LDSK + kk +
-                                         8 * (lane >> 4));
+            for (int b = 0; b < 2; ++b) {
+                const int rb = wn * 32 + b * 16 + r16;
+                fb[b] = *(const bf16x8*)(Bt + rb * 128 + ((c ^ ((rb >> 1) & 7)) << 4));
             }
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a) {
+                const int ra = wm * 64 + a * 16 + r16;
+                const bf16x8 fa = *(const bf16x8*)(At + ra * 128 + ((c ^ ((ra >> 1) & 7)) << 4));
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0,
-                                                                        0, 0);
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[b], acc[a][b], 0, 0, 0);
+            }
         }
     }
+    wait_vmcnt<0>();  // no load may still target LDS when the workgroup ends
     // D tile layout: lane l holds rows 4*(l/16)+i, column l%16
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int col = n0 + wn * 64 + b * 16 + (lane & 15);
+        for (int b = 0; b < 2; ++b) {
+            const int col = n0 + wn * 32 + b * 16 + r16;
             if (col >= N) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = m0 + wm * 64 + a * 16 + 4 * (lane >> 4) + i;
+                const int row = m0 + wm * 64 + a * 16 + 4 * g + i;
                 if (row >= M) continue;
                 if (MODE == 3) {
                     ((float*)out)[((size_t)blockIdx.z * M + row) * N + col] = acc[a][b][i];
@@ -154,23 +207,30 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(int M, int N, int S,
 hipError_t launch_gemm(int M, int N, int K, const void* x, const void* w, void* out,
                        const void* add, int mode, void* scratch, hipStream_t s) {
     const Split sp = choose_split(M, N, K);
-    const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, sp.S);
     const uint16_t* xa = (const uint16_t*)x;
     const uint16_t* wa = (const uint16_t*)w;
+    const dim3 grid((N + GEMM_BN - 1) / GEMM_BN, (M + GEMM_BM - 1) / GEMM_BM, sp.S);
+    const dim3 blk(256);
     if (sp.S == 1) {
-        if (mode == 0) hipLaunchKernelGGL(k_gemm<0>, grid, dim3(256), 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
-        else if (mode == 1) hipLaunchKernelGGL(k_gemm<1>, grid, dim3(256), 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
-        else hipLaunchKernelGGL(k_gemm<2>, grid, dim3(256), 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
+        if (mode == 0)
+            hipLaunchKernelGGL((k_gemm<0, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
+        else if (mode == 1)
+            hipLaunchKernelGGL((k_gemm<1, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
+        else
+            hipLaunchKernelGGL((k_gemm<2, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_gemm<3>, grid, dim3(256), 0, s, M, N, K, sp.kchunk, xa, wa, scratch,
-                       (const void*)nullptr);
+    hipLaunchKernelGGL((k_gemm<3, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa,
+                       scratch, (const void*)nullptr);
     const size_t total = (size_t)M * N;
     const int blocks = (int)((total + 255) / 256);
     const float* part = (const float*)scratch;
-    if (mode == 0) hipLaunchKernelGGL(k_splitk_reduce<0>, dim3(blocks), dim3(256), 0, s, M, N, sp.S, part, out, add);
-    else if (mode == 1) hipLaunchKernelGGL(k_splitk_reduce<1>, dim3(blocks), dim3(256), 0, s, M, N, sp.S, part, out, add);
-    else hipLaunchKernelGGL(k_splitk_reduce<2>, dim3(blocks), dim3(256), 0, s, M, N, sp.S, part, out, add);
+    if (mode == 0)
+        hipLaunchKernelGGL(k_splitk_reduce<0>, dim3(blocks), blk, 0, s, M, N, sp.S, part, out, add);
+    else if (mode == 1)
+        hipLaunchKernelGGL(k_splitk_reduce<1>, dim3(blocks), blk, 0, s, M, N, sp.S, part, out, add);
+    else
+        hipLaunchKernelGGL(k_splitk_reduce<2>, dim3(blocks), blk, 0, s, M, N, sp.S, part, out, add);
     return hipGetLastError();
 }
 

@@ -23,6 +23,43 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 DENSE_BYTES = 379_857_408          # router + shared gate_up + shared down + latent down + up + norm + bias
 EXPERT_BYTES = 2_924_544           # one MXFP4 expert: W13 + scales + W2 + scales
+UP_EXPERT_BYTES = 1_949_696        # W13 [1024, 3584] MXFP4 + E8M0 scales
+DOWN_EXPERT_BYTES = 974_848        # W2 [3584, 512] MXFP4 + E8M0 scales
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ffn_up_fast_T256_uniform_traffic.md")
+KERNEL_SOURCES = ["mixture_experts_decode_gemm_amd/csrc/ffn.hip",
+                  "mixture_experts_decode_gemm_amd/csrc/device.h"]
+
+
+def source_digest():
+    """Hash of the gate/up kernel's sources with comments and blank space removed, so that
+    only a change of code (not of its comments) retires the recorded counters."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(T, zipf):
+    """HBM bytes per launch of the gate/up kernel from the committed PMC summary (FETCH_SIZE
+    and WRITE_SIZE, each scaled by the same counter's reading for a copy of known size), or
+    None when there is none for this workload or the kernel's source changed since."""
+    if T != 256 or zipf or not os.path.exists(TRAFFIC_FILE):
+        return None
+    import re
+    m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_FILE).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def parse():
@@ -33,7 +70,10 @@ def parse():
     p.add_argument("--tokens", type=int, default=256)
     p.add_argument("--zipf", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=160)
+    p.add_argument("--cpu-tokens", type=int, default=192)
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
+                   help="finish with one plain copy kernel of this many MiB (read and written), "
+                        "the reference for scaling the HBM byte counters")
     p.add_argument("--sweep", action="store_true", help="also time T in {65,130,255,510,1020}")
     return p.parse_args()
 
@@ -100,27 +140,42 @@ def main():
           f"{layer_gbs:.0f} GB/s = {100 * layer_gbs / HBM_PEAK_GBS:.1f}% of HBM", file=sys.stderr,
           flush=True)
 
-    # the dominant kernel: the grouped expert FFN (its two launches, up and down) timed with
-    # HIP events on its launch stream, fed the layer's own codes, lists and units
+    # the dominant kernel: the grouped FFN's gate/up pass (one launch of k_ffn_up_fast),
+    # timed with HIP events on its launch stream and fed the layer's own codes, lists and
+    # units; then the down pass and the whole grouped FFN the same way
     rows = torch.empty(T * 16, 3584, dtype=torch.bfloat16, device="cuda")
     fws = torch.empty(moe.moe_ffn_workspace_size(d), dtype=torch.uint8, device="cuda")
-    units = v["units_raw"]
-    ffn_args = (d, dw["w13"], dw["s13"], dw["w2"], dw["s2"], v["codes"], v["scales"], v["pairs"],
-                units, v["num_units"], rows, fws)
-    for _ in range(3):
-        moe.moe_grouped_ffn(*ffn_args, stream=stream)
-    torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for _ in range(a.steps):
-        moe.moe_grouped_ffn(*ffn_args, stream=stream)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    ffn_ms = f0.elapsed_time(f1) / a.steps
-    # algorithmic bytes of one grouped-FFN call: each touched expert's MXFP4 weights once,
-    # the MXFP8 latent (codes + scales) once, the BF16 expanded rows written once
-    ffn_bytes = D * EXPERT_BYTES + T * 3584 * 33 // 32 + T * 16 * 3584 * 2
-    ffn_gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    ffn_w = (d, dw["w13"], dw["s13"], dw["w2"], dw["s2"])
+    lists = (v["pairs"], v["units_raw"], v["num_units"])
+
+    def time_stage(stages):
+        def call():
+            moe.moe_grouped_ffn_stages(*ffn_w, v["codes"], v["scales"], *lists, rows, fws,
+                                       stages, stream=stream)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(a.steps):
+            call()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        return f0.elapsed_time(f1) / a.steps * 1e3
+
+    moe.moe_grouped_ffn_stages(*ffn_w, v["codes"], v["scales"], *lists, rows, fws, moe.MOE_FFN_UP,
+                               stream=stream)
+    up_us = time_stage(moe.MOE_FFN_UP)
+    down_us = time_stage(moe.MOE_FFN_DOWN)
+    ffn_us = time_stage(moe.MOE_FFN_UP | moe.MOE_FFN_DOWN)
+    # algorithmic bytes per launch: each touched expert's W13 (+ scales) once, the MXFP8
+    # latent once, the MXFP8 hidden of every pair written once (up); each touched expert's
+    # W2 (+ scales) once, the hidden read once, the BF16 rows written once (down)
+    hid_bytes = T * 16 * 512 * 33 // 32
+    up_bytes = D * UP_EXPERT_BYTES + T * 3584 * 33 // 32 + hid_bytes
+    down_bytes = D * DOWN_EXPERT_BYTES + hid_bytes + T * 16 * 3584 * 2
+    up_gbs = up_bytes / up_us / 1e3
+    traffic = recorded_traffic(T, a.zipf)
 
     res = {
         "metric": "MoE-layer decode tokens/s at 256 tokens; % of HBM roofline (GB/s achieved)",
@@ -142,10 +197,14 @@ def main():
         "layer_roofline": {"bound": "hbm", "weight_bytes": layer_bytes,
                            "achieved": layer_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": layer_gbs / HBM_PEAK_GBS},
-        "roofline": {"kernel": "moe_grouped_ffn (k_ffn_up_mx + k_ffn_down_mx)", "bound": "hbm",
-                     "achieved": ffn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ffn_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": ffn_bytes, "us_per_launch": ffn_ms * 1e3},
+        "roofline": {"kernel": "k_ffn_up_fast (gate/up pass of the grouped expert FFN)",
+                     "bound": "hbm", "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": up_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "bytes_per_launch": up_bytes, "us_per_launch": up_us},
+        "ffn_down": {"kernel": "k_ffn_down_fast", "us_per_launch": down_us,
+                     "bytes_per_launch": down_bytes, "achieved_gbs": down_bytes / down_us / 1e3},
+        "grouped_ffn": {"us_per_call": ffn_us, "bytes_per_call": up_bytes + down_bytes,
+                        "achieved_gbs": (up_bytes + down_bytes) / ffn_us / 1e3},
     }
     if a.sweep:
         sweep = {}
@@ -170,6 +229,14 @@ def main():
                                "kind": "oracle",
                                "sample": f"the oracle layer on the first {n} of the {T} tokens "
                                          f"(same weights and inputs), {sec:.1f} s"}
+    if a.copy_probe:
+        n = a.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_probe MiB
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = n * 4
     print(json.dumps(res), flush=True)
 
 

@@ -150,6 +150,20 @@ moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const
                            void* workspace, size_t ws_bytes, void* stream);
 size_t moe_ffn_workspace_size(const moe_dims* d);
 
+/* One pass of the grouped FFN above (MXFP4 x MXFP8 experts only), for callers that time
+   or schedule the two expert passes apart.  stages = MOE_FFN_UP: steps (1)-(3) of the
+   expert computation (gate/up product, SiLU-and-mul, MXFP8 hidden into the workspace at
+   the offsets stated above; rows untouched, may be NULL); MOE_FFN_DOWN: step (4), rows
+   from the hidden a previous MOE_FFN_UP call left in the same workspace with the same
+   lists (act and act_scales unused, may be NULL); MOE_FFN_UP | MOE_FFN_DOWN: the same as
+   moe_grouped_ffn.  Other values, or the BF16 format with a single stage: MOE_ERR_FORMAT. */
+enum { MOE_FFN_UP = 1, MOE_FFN_DOWN = 2 };
+moe_status moe_grouped_ffn_stages(const moe_dims* d, const moe_expert_weights* w,
+                                  const void* act, const uint8_t* act_scales,
+                                  const int32_t* pairs, const moe_unit* units,
+                                  const int32_t* num_units, void* rows, void* workspace,
+                                  size_t ws_bytes, int32_t stages, void* stream);
+
 /* Finalize ([wide] Finalize): out[t,c] = BF16_RNE(acc), acc = +0 then
    acc = fma(w[t,k], rows[K t + k, c], acc) for k = 0..K-1 in order, FP32.  ids may be
    NULL; when given, a slot with ids[t,k] < 0 is skipped and its row never read ([fp]:
@@ -176,7 +190,7 @@ moe_status moe_linear(int32_t M, int32_t N, int32_t K, const void* x, const void
 size_t moe_linear_workspace_size(int32_t M, int32_t N, int32_t K);
 
 /* Shared-expert gated activation ([ep] EpMoeLayer.gate_up; SiLU-and-mul stands in for
-   the pages' undefined "SiTU"): out[m,j] = BF16(silu(gu[m,j]) * gu[m,S+j]), FP32 math;
+   the pages' undefined SiTU): out[m,j] = BF16(silu(gu[m,j]) * gu[m,S+j]), FP32 math;
    gu [M, 2S], out [M, S] BF16; S % 8 == 0. */
 moe_status moe_silu_mul(int32_t M, int32_t S, const void* gu, void* out, void* stream);
 

@@ -51,7 +51,7 @@ class moe_layer_weights(C.Structure):
 
 
 EXPORTS = ["moe_router_topk", "moe_router_workspace_size", "moe_build_lists",
-           "moe_lists_workspace_size", "moe_quant_mxfp8", "moe_grouped_ffn",
+           "moe_lists_workspace_size", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_stages",
            "moe_ffn_workspace_size", "moe_finalize", "moe_rmsnorm", "moe_linear",
            "moe_linear_workspace_size", "moe_silu_mul", "moe_layer", "moe_workspace_size",
            "moe_workspace_layout", "moe_version"]
@@ -76,6 +76,8 @@ def lib():
             "moe_lists_workspace_size": (sz, [D]),
             "moe_quant_mxfp8": (i32, [i32, i32, v, v, v, v]),
             "moe_grouped_ffn": (i32, [D, C.POINTER(moe_expert_weights), v, v, v, v, v, v, v, sz, v]),
+            "moe_grouped_ffn_stages": (i32, [D, C.POINTER(moe_expert_weights), v, v, v, v, v, v, v,
+                                             sz, i32, v]),
             "moe_ffn_workspace_size": (sz, [D]),
             "moe_finalize": (i32, [i32, i32, i32, v, v, v, v, v]),
             "moe_rmsnorm": (i32, [i32, i32, v, v, f, v, v]),
@@ -206,6 +208,23 @@ def moe_grouped_ffn(d, w13, s13, w2, s2, act, act_scales, pairs, units, num_unit
                                _ptr(rows, BF16, "rows"), _ptr(workspace, U8, "workspace"),
                                workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("moe_grouped_ffn", st)
+
+
+MOE_FFN_UP, MOE_FFN_DOWN = 1, 2
+
+
+def moe_grouped_ffn_stages(d, w13, s13, w2, s2, act, act_scales, pairs, units, num_units, rows,
+                           workspace, stages, stream=None):
+    """One or both passes of the grouped FFN (MOE_FFN_UP, MOE_FFN_DOWN or their OR)."""
+    w = expert_weights(w13, s13, w2, s2)
+    st = lib().moe_grouped_ffn_stages(C.byref(d), C.byref(w), _ptr(act, (U8, BF16), "act"),
+                                      _ptr(act_scales, U8, "act_scales"),
+                                      _ptr(pairs, I32, "pairs"), _ptr(units, I32, "units"),
+                                      _ptr(num_units, I32, "num_units"), _ptr(rows, BF16, "rows"),
+                                      _ptr(workspace, U8, "workspace"),
+                                      workspace.numel() if workspace is not None else 0,
+                                      int(stages), _stream(stream))
+    _check("moe_grouped_ffn_stages", st)
 
 
 def moe_finalize(rows, weights, out, ids=None, stream=None):

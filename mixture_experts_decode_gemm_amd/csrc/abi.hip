@@ -150,23 +150,29 @@ size_t moe_ffn_workspace_size(const moe_dims* d) {
     return ffn_scratch_bytes(d->max_tokens * d->top_k, d->expert_inter);
 }
 
-moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const void* act,
-                           const uint8_t* act_scales, const int32_t* pairs,
-                           const moe_unit* units, const int32_t* num_units, void* rows,
-                           void* workspace, size_t ws_bytes, void* stream) {
+moe_status moe_grouped_ffn_stages(const moe_dims* d, const moe_expert_weights* w,
+                                  const void* act, const uint8_t* act_scales,
+                                  const int32_t* pairs, const moe_unit* units,
+                                  const int32_t* num_units, void* rows, void* workspace,
+                                  size_t ws_bytes, int32_t stages, void* stream) {
     moe_status st = check_dims(d);
     if (st != MOE_OK) return st;
-    if (!w || !w->w13 || !w->w2 || !act || !pairs || !units || !num_units || !rows)
-        return MOE_ERR_NULL;
+    if (stages < 1 || stages > 3) return MOE_ERR_FORMAT;
     const bool mx = d->expert_format == MOE_FMT_MXFP4_MXFP8;
-    if (mx && (!w->s13 || !w->s2 || !act_scales || !workspace)) return MOE_ERR_NULL;
-    if (!al16(w->w13) || !al16(w->w2) || !al16(act) || !al16(pairs) || !al16(units) ||
-        !al16(num_units) || !al16(rows))
-        return MOE_ERR_ALIGN;
-    if (mx && (!al16(w->s13) || !al16(w->s2) || !al16(act_scales) || !al16(workspace)))
+    if (!mx && stages != 3) return MOE_ERR_FORMAT;
+    const bool up = stages & MOE_FFN_UP, down = stages & MOE_FFN_DOWN;
+    if (!w || !pairs || !units || !num_units) return MOE_ERR_NULL;
+    if ((up && (!w->w13 || !act)) || (down && (!w->w2 || !rows))) return MOE_ERR_NULL;
+    if (!al16(pairs) || !al16(units) || !al16(num_units)) return MOE_ERR_ALIGN;
+    if ((up && (!al16(w->w13) || !al16(act))) || (down && (!al16(w->w2) || !al16(rows))))
         return MOE_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     if (mx) {
+        if ((up && (!w->s13 || !act_scales)) || (down && !w->s2) || !workspace)
+            return MOE_ERR_NULL;
+        if ((up && (!al16(w->s13) || !al16(act_scales))) || (down && !al16(w->s2)) ||
+            !al16(workspace))
+            return MOE_ERR_ALIGN;
         if (ws_bytes < ffn_scratch_bytes(d->tokens * d->top_k, d->expert_inter))
             return MOE_ERR_WORKSPACE;
         uint8_t* hid = (uint8_t*)workspace;
@@ -175,11 +181,19 @@ moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const
             d->tokens, d->top_k, d->experts, d->latent, d->expert_inter, d->unit_tokens,
             (const uint8_t*)w->w13, (const uint8_t*)w->s13, (const uint8_t*)w->w2,
             (const uint8_t*)w->s2, (const uint8_t*)act, act_scales, pairs, (const int32_t*)units,
-            num_units, rows, hid, hsc, s));
+            num_units, rows, hid, hsc, stages, s));
     }
     return launch_status(launch_ffn_bf16(d->tokens, d->top_k, d->experts, d->latent,
                                          d->expert_inter, d->unit_tokens, w->w13, w->w2, act,
                                          pairs, (const int32_t*)units, num_units, rows, s));
+}
+
+moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const void* act,
+                           const uint8_t* act_scales, const int32_t* pairs,
+                           const moe_unit* units, const int32_t* num_units, void* rows,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    return moe_grouped_ffn_stages(d, w, act, act_scales, pairs, units, num_units, rows,
+                                  workspace, ws_bytes, MOE_FFN_UP | MOE_FFN_DOWN, stream);
 }
 
 moe_status moe_finalize(int32_t tokens, int32_t top_k, int32_t cols, const void* rows,
@@ -297,7 +311,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_ffn_mx(T, K, E, L, I, d->unit_tokens, (const uint8_t*)w->experts.w13,
                               (const uint8_t*)w->experts.s13, (const uint8_t*)w->experts.w2,
                               (const uint8_t*)w->experts.s2, codes, scales, pairs, units, nu,
-                              rows, hid, hid_scales, s));
+                              rows, hid, hid_scales, 3, s));
     } else {
         MOE_TRY(launch_ffn_bf16(T, K, E, L, I, d->unit_tokens, w->experts.w13, w->experts.w2,
                                 latent, pairs, units, nu, rows, s));

@@ -1,7 +1,8 @@
-// ffn.hip -- the grouped expert FFN over unit windows (wide page, module summary: "the
-// listed wide grouped engine ... every touched expert streams once per 8 of its tokens",
-// precision: "MXFP8 activations x MXFP4 experts with the MXFP8 hidden"; ep/layer page,
-// EpRouted: MXFP4 x MXFP8 experts with the gated activation).
+// ffn.hip -- the grouped expert FFN over unit windows (wide page, module summary: the
+// grouped expert engine over the routing lists, whose cost is one pass over each touched
+// expert's weights per window of 8 of its tokens; precision paragraph: MXFP8 activations,
+// MXFP4 experts, an MXFP8 hidden; ep/layer page, EpRouted: MXFP4 x MXFP8 experts with
+// the gated activation).
 //
 // CDNA4 path: V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the weights as the A operand
 // (16 weight rows x 128 K, E2M1, E8M0 per 32) and the unit's tokens as the B operand
@@ -527,14 +528,14 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const uint8_t* s13, const uint8_t* w2, const uint8_t* s2,
                          const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
                          const int32_t* units, const int32_t* num_units, void* rows,
-                         uint8_t* hid, uint8_t* hsc, hipStream_t s) {
+                         uint8_t* hid, uint8_t* hsc, int stages, hipStream_t s) {
     (void)T;
     (void)unit;
     const int4* un = (const int4*)units;
     const int up_items = E * (I / UP_COLS);  // an upper bound: the kernels read D on the device
     const int cus = num_cus();
     const dim3 blk(256);
-    switch (L % 512 == 0 ? L / 512 : 0) {
+    switch ((stages & 1) ? (L % 512 == 0 ? L / 512 : 0) : -1) {
 #define MOE_UP(SPW)                                                                          \
     case SPW:                                                                                \
         hipLaunchKernelGGL(k_ffn_up_fast<SPW>, dim3(up_items < cus ? up_items : cus), blk, 0, \
@@ -542,6 +543,8 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
         break;
         MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7)
 #undef MOE_UP
+        case -1:
+            break;
         default:
             hipLaunchKernelGGL(k_ffn_up_generic, dim3(persistent_blocks(up_items, 8)), blk, 0, s,
                                K, L, I, w13, s13, codes, scales, pairs, un, num_units, hid, hsc);
@@ -549,7 +552,7 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     const int MTsel = L % 512 == 0 ? 8 : (L % 256 == 0 ? 4 : 0);
     const int down_items = MTsel ? E * (L / (64 * MTsel)) : E * (L / DOWN_ROWS);
     const int dgrid = down_items < cus ? down_items : cus;
-    switch (MTsel * 10 + I / 128) {
+    switch ((stages & 2) ? MTsel * 10 + I / 128 : -1) {
 #define MOE_DOWN(MT, IS)                                                                     \
     case MT * 10 + IS:                                                                       \
         hipLaunchKernelGGL((k_ffn_down_fast<IS, MT>), dim3(dgrid), blk, 0, s, L, w2, s2, hid,  \
@@ -558,6 +561,8 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
         MOE_DOWN(8, 1) MOE_DOWN(8, 2) MOE_DOWN(8, 4) MOE_DOWN(4, 1) MOE_DOWN(4, 2)
         MOE_DOWN(4, 4)
 #undef MOE_DOWN
+        case -1:
+            break;
         default:
             hipLaunchKernelGGL(k_ffn_down_generic, dim3(persistent_blocks(down_items, 8)), blk, 0,
                                s, L, I, w2, s2, hid, hsc, pairs, un, num_units, (uint16_t*)rows);

@@ -4,7 +4,8 @@
 //
 // MI355X layout: one thread per 8 consecutive columns of one token (16-byte loads and
 // stores); all K row fragments of a thread are loaded before the first FMA, so each
-// lane keeps K 16-byte loads in flight (the pages' "every load in flight first").
+// lane keeps K 16-byte loads in flight (the Finalize section issues all of its loads
+// before the first multiply-add).
 // Threads are numbered token-major so a wavefront streams 64 x 16 B = 1 KiB of one row.
 #include "device.h"
 #include "kernels.h"

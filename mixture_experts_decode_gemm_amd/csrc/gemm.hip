@@ -1,6 +1,7 @@
 // gemm.hip -- dense BF16 linears out = x W^T with FP32 accumulation (wide page, module
-// summary: "BF16 linears", "FP32 router logits", "the latent rounded once to BF16";
-// ep/layer page, stock_order and the "cuBLAS addmm: one rounding" of the up-projection).
+// summary, precision paragraph: BF16 dense projections, router logits in FP32, the
+// latent rounded to BF16 once; ep/layer page, stock_order, and the single rounding of
+// the up-projection added into the shared partial).
 //
 // Decode shapes are skinny (M = tokens, 65..1020) and wide (N up to 12288, K up to 7168):
 // the weights must stream from HBM at full rate, which takes many bytes in flight per CU.

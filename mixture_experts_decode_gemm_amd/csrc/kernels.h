@@ -24,13 +24,14 @@ hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32
                         void* scratch, hipStream_t s);
 
 // grouped FFN: MXFP4 x MXFP8; the MXFP8 hidden goes to hid [T*K, I] and hid_scales
-// [T*K, I/32] (by pair id); ffn_scratch_bytes(P, I) covers both, 256-aligned
+// [T*K, I/32] (by pair id); ffn_scratch_bytes(P, I) covers both, 256-aligned.
+// stages: bit 0 the gate/up pass, bit 1 the down pass
 size_t ffn_scratch_bytes(int P, int I);
 hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint8_t* w13,
                          const uint8_t* s13, const uint8_t* w2, const uint8_t* s2,
                          const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
                          const int32_t* units, const int32_t* num_units, void* rows,
-                         uint8_t* hid, uint8_t* hid_scales, hipStream_t s);
+                         uint8_t* hid, uint8_t* hid_scales, int stages, hipStream_t s);
 hipError_t launch_ffn_bf16(int T, int K, int E, int L, int I, int unit, const void* w13,
                            const void* w2, const void* latent, const int32_t* pairs,
                            const int32_t* units, const int32_t* num_units, void* rows,

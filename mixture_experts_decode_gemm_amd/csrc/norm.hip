@@ -1,7 +1,7 @@
 // norm.hip -- latent RMSNorm (ep/layer page, EpMoeLayer: ops.rms_norm(normed, routed,
 // norm, eps); wide page, WideMoE.tail: the RMSNorm fused into the latent all-reduce) and
 // the shared expert's gated activation (ep/layer page, EpMoeLayer.gate_up: the [T, 2S]
-// gate_up rows; SiLU-and-mul stands in for the pages' undefined "SiTU").
+// gate_up rows; SiLU-and-mul stands in for the pages' undefined SiTU).
 #include "device.h"
 #include "kernels.h"
 

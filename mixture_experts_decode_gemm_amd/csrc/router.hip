@@ -1,6 +1,6 @@
 // router.hip -- sigmoid top-K routing (ep/layer page, EpMoeLayer.topk: the stock
 // router's sigmoid top-16 over one group with the correction bias, renormalize and
-// scale; wide page, WideRoute: "exact top16 and renormalized weights").
+// scale; wide page, WideRoute: an exact top-16 with renormalised weights).
 //
 // One wavefront per token.  Each lane owns experts lane, lane+64, ... (<= 16 per lane,
 // E <= 1024) and builds 64-bit selection keys (order-preserving bits of the FP32 key

@@ -10,7 +10,7 @@
  * Build: gcc -O2 -ffp-contract=off -fopenmp (no fast-math).  Every dot product is
  * accumulated in double and rounded once; every rounding is round-to-nearest-even.
  *
- * Sources ("the pages"):
+ * Sources (the pages):
  *   [wide]     vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.moe.wide
  *   [ep]       vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.moe.ep.layer
  *   [finalize] vllm.models.glm5next.nvidia.specialized_decode.cutedsl.finalize_publish
@@ -73,9 +73,9 @@ uint16_t orc_f32_to_bf16(float f) {
 
 static uint16_t bf16_of(double v) { return orc_f32_to_bf16((float)v); }
 
-/* OCP MX v1.0 element formats (BASELINE configuration: "E4M3, E8M0 scale per 32",
-   "E2M1"); the pages name the formats ("MXFP8 activations x MXFP4 experts", [wide]
-   module summary, precision paragraph) but print no codec. */
+/* OCP MX v1.0 element formats: E4M3 and E2M1 elements, one E8M0 scale per 32.  The
+   pages name MXFP8 activations and MXFP4 expert weights ([wide] module summary,
+   precision paragraph) but print no codec. */
 double orc_e4m3_value(uint8_t c) {
     int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
     if (e == 15 && m == 7) return NAN;
@@ -114,8 +114,9 @@ double orc_e8m0_value(uint8_t b) {
 
 /* ============================ routing ============================================ */
 
-/* The pages route with the stock sigmoid top-16 ([ep] EpMoeLayer.topk: one group,
-   "sigmoid", correction bias, renormalize, scale) but never state the exponential.
+/* The pages route with the stock sigmoid top-16 ([ep] EpMoeLayer.topk: one group, a
+   sigmoid score, the correction bias, renormalisation, the routed scale) but never
+   state the exponential.
    Routing ids must be bit-exact across implementations, so the exponential is
    defined here from a textbook method (Cody and Waite's argument reduction
    z = n ln2 + r with ln2 split into a 16-significant-bit head and a tail, then the
@@ -165,8 +166,8 @@ float orc_sigmoid(float logit) {
     return 1.0f / den;
 }
 
-/* router logits, FP32 out ([wide] module summary: "FP32 router logits"; [ep]
-   stock_order: mm(x, gate.T, out_dtype=float32)) */
+/* router logits with an FP32 output ([wide] module summary, precision paragraph;
+   [ep] stock_order, where the router product is taken straight to FP32) */
 void orc_linear_f32(int M, int N, int K, const uint16_t* x, const uint16_t* w, float* out) {
 #pragma omp parallel for collapse(2) schedule(static)
     for (int m = 0; m < M; ++m)
@@ -293,8 +294,8 @@ int orc_build_lists(int T, int K, int E, int unit_tokens, const int32_t* ids, in
 
 /* ============================ MXFP8 quantisation ================================== */
 
-/* One 32-element block ([wide] module summary: the latent "written as the experts'
-   MXFP8 plan", "MXFP8 activations ... with the MXFP8 hidden").  The pages name the
+/* One 32-element block ([wide] module summary: the latent becomes the experts' MXFP8
+   input, and the expert hidden is MXFP8 as well).  The pages name the
    quantiser but not its scale rule; this is the OCP MX v1.0 rule: shared exponent
    X = floor(log2(amax)) - 8 (8 = the largest E4M3 exponent), clamped to the E8M0
    range, elements v / 2^X rounded to the nearest E4M3 value with saturation.  An
@@ -357,11 +358,11 @@ static void dequant_mxfp8_row(const uint8_t* codes, const uint8_t* sc, int n, do
     for (int j = 0; j < n; ++j) out[j] = orc_e4m3_value(codes[j]) * orc_e8m0_value(sc[j / 32]);
 }
 
-/* First half of one expert on one pair ([wide] module summary: "the listed wide
-   grouped engine"; [ep] EpRouted, the stock MXFP4 x MXFP8 routed MoE with its gated
-   activation): h = A W13^T over the dequantised MXFP8 latent row of token p/K
+/* First half of one expert on one pair ([wide] module summary, the grouped expert
+   engine over the routing lists; [ep] EpRouted, the stock MXFP4 x MXFP8 routed MoE with
+   its gated activation): h = A W13^T over the dequantised MXFP8 latent row of token p/K
    (FP32 from a double sum), act = silu(gate) * up on the two halves (gate first),
-   then act is quantised to MXFP8 from FP32.  The pages' gated activation ("SiTU") is
+   then act is quantised to MXFP8 from FP32.  The pages' gated activation (SiTU) is
    never defined; SiLU-and-mul is used -- parity unpinned against the pages. */
 void orc_ffn_up_mx(int n, const int32_t* pair_ids, const int32_t* pair_experts, int K, int L, int I,
                    const uint8_t* codes, const uint8_t* scales, const uint8_t* w13,
@@ -485,8 +486,9 @@ void orc_rmsnorm(int T, int cols, const uint16_t* r, const uint16_t* g, float ep
 
 /* ============================ dense linears ====================================== */
 
-/* BF16 linear with FP32 accumulation and one BF16 rounding ([wide] module summary:
-   "BF16 linears", "the latent rounded once to BF16") */
+/* BF16 linear with FP32 accumulation and one BF16 rounding ([wide] module summary,
+   precision paragraph: the dense projections are BF16, and the latent is rounded to
+   BF16 once) */
 void orc_linear_bf16(int M, int N, int K, const uint16_t* x, const uint16_t* w, uint16_t* out) {
 #pragma omp parallel for collapse(2) schedule(static)
     for (int m = 0; m < M; ++m)
@@ -500,7 +502,8 @@ void orc_linear_bf16(int M, int N, int K, const uint16_t* x, const uint16_t* w, 
 }
 
 /* [ep] EpMoeLayer: shared.addmm_(normed, up.T) -- the up-projection added into the
-   BF16 shared partial with one rounding ("cuBLAS addmm: one rounding, as stock"). */
+   BF16 shared partial with one rounding, as the stock path does (the [ep] module
+   summary notes the single rounding of the library addmm). */
 void orc_linear_add_bf16(int M, int N, int K, const uint16_t* x, const uint16_t* w,
                          const uint16_t* add, uint16_t* out) {
 #pragma omp parallel for collapse(2) schedule(static)
@@ -517,7 +520,7 @@ void orc_linear_add_bf16(int M, int N, int K, const uint16_t* x, const uint16_t*
 
 /* [ep] EpMoeLayer.gate_up / stock_order: the stock gated activation on the [T, 2S]
    gate_up rows, gate in the first half.  SiLU-and-mul stands in for the undefined
-   "SiTU" (parity unpinned against the pages). */
+   SiTU (parity unpinned against the pages). */
 void orc_silu_mul_bf16(int M, int S, const uint16_t* gu, uint16_t* out) {
 #pragma omp parallel for schedule(static)
     for (int m = 0; m < M; ++m)

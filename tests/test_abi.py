@@ -123,6 +123,20 @@ def test_lists_and_ffn_reject(L):
                              None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_grouped_ffn(C.byref(d), C.byref(w), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                              1 << 30, None) == moe.MOE_ERR_NULL
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
+    for bad in (0, 4, -1):
+        assert L.moe_grouped_ffn_stages(C.byref(d), C.byref(w), *args, bad,
+                                        None) == moe.MOE_ERR_FORMAT
+    # the down pass alone needs no activations; the up pass alone no rows
+    assert L.moe_grouped_ffn_stages(C.byref(d), C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, 16, moe.MOE_FFN_UP, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_grouped_ffn_stages(C.byref(d), C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                    FAKE, 16, moe.MOE_FFN_DOWN, None) == moe.MOE_ERR_NULL
+    assert L.moe_grouped_ffn_stages(C.byref(d), C.byref(w), None, None, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, 16, moe.MOE_FFN_DOWN, None) == moe.MOE_ERR_WORKSPACE
+    d.expert_format = moe.MOE_FMT_BF16
+    assert L.moe_grouped_ffn_stages(C.byref(d), C.byref(w), *args, moe.MOE_FFN_UP,
+                                    None) == moe.MOE_ERR_FORMAT
 
 
 def test_linear_rmsnorm_silu_reject(L):

@@ -95,6 +95,28 @@ def test_ffn_mx_full_size_multi_unit(orc):
     check_mx(orc, d, w, codes, scales, ids, sample)
 
 
+def test_ffn_stages_match_grouped():
+    """The up pass then the down pass, as two calls, give the one-call result bit for bit."""
+    T, K, E, L, I = 40, 4, 12, 512, 256
+    dd = dict(L=L, I=I, E=E, expert_format=0)
+    w = syn.expert_weights(dd, seed=2)
+    codes, scales = syn.mxfp8_random(syn.rng(2, 702), T, L)
+    ids = random_ids(np.random.default_rng(7), T, K, E)
+    d = moe.dims(T, T, hidden=256, latent=L, experts=E, top_k=K, expert_inter=I)
+    ref_rows, ref_hid, ref_hsc = run_ffn_mx(d, w, codes, scales, ids)
+    pairs, units, nu = build_lists(d, dev(ids))
+    rows = torch.zeros(T * K, L, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(moe.moe_ffn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    args = (d, dev(w["w13"]), dev(w["s13"]), dev(w["w2"]), dev(w["s2"]))
+    moe.moe_grouped_ffn_stages(*args, dev(codes), dev(scales), pairs, units, nu, None, ws,
+                               moe.MOE_FFN_UP)
+    moe.moe_grouped_ffn_stages(*args, None, None, pairs, units, nu, rows, ws, moe.MOE_FFN_DOWN)
+    torch.cuda.synchronize()
+    P = T * K
+    assert np.array_equal(host(ws[:P * I]).reshape(P, I), ref_hid)
+    assert np.array_equal(host(rows), ref_rows)
+
+
 def test_ffn_bf16_toy(orc):
     d0 = dict(syn.TOY)
     T, K, E, L, I = d0["T"], d0["K"], d0["E"], d0["L"], d0["I"]

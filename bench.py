@@ -46,11 +46,11 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(T, zipf):
+def recorded_traffic(T, zipf, row_major):
     """HBM bytes per launch of the gate/up kernel from the committed PMC summary (FETCH_SIZE
     and WRITE_SIZE, each scaled by the same counter's reading for a copy of known size), or
     None when there is none for this workload or the kernel's source changed since."""
-    if T != 256 or zipf or not os.path.exists(TRAFFIC_FILE):
+    if T != 256 or zipf or row_major or not os.path.exists(TRAFFIC_FILE):
         return None
     import re
     m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_FILE).read(), re.S)
@@ -75,6 +75,8 @@ def parse():
                    help="finish with one plain copy kernel of this many MiB (read and written), "
                         "the reference for scaling the HBM byte counters")
     p.add_argument("--sweep", action="store_true", help="also time T in {65,130,255,510,1020}")
+    p.add_argument("--row-major", action="store_true",
+                   help="run the experts on the row-major weights instead of the packed layout")
     return p.parse_args()
 
 
@@ -105,17 +107,23 @@ def main():
 
     dw = {k: dev(v) for k, v in w.items() if v is not None}
     xd = dev(x)
+    fmt = moe.MOE_FMT_MXFP4_MXFP8
+    if not a.row_major:  # load-time preparation of the expert weights, outside any timing
+        pk = moe.moe_pack_expert_weights(moe.dims(1, 1), dw["w13"], dw["s13"], dw["w2"], dw["s2"])
+        dw.update(w13=pk[0], s13=pk[1], w2=pk[2], s2=pk[3])
+        fmt = moe.MOE_FMT_MXFP4_MXFP8_PACKED
+        torch.cuda.synchronize()
     print(f"# inputs generated and resident in HBM in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
     lw = moe.layer_weights(dw["w_gate"], dw["bias"], dw["w_down"], dw["w_shared_gu"],
                            dw["w_shared_dn"], dw["norm_w"], dw["w_up"], dw["w13"], dw["s13"],
                            dw["w2"], dw["s2"])
-    dmax = moe.dims(1020, 1020)
+    dmax = moe.dims(1020, 1020, expert_format=fmt)
     ws = torch.zeros(moe.moe_workspace_size(dmax), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def run_T(t, steps, warmup):
-        d = moe.dims(t, 1020)
+        d = moe.dims(t, 1020, expert_format=fmt)
         xin = xd[:t].contiguous()
         out = torch.empty(t, 7168, dtype=torch.bfloat16, device="cuda")
         for _ in range(warmup):
@@ -175,7 +183,7 @@ def main():
     up_bytes = D * UP_EXPERT_BYTES + T * 3584 * 33 // 32 + hid_bytes
     down_bytes = D * DOWN_EXPERT_BYTES + hid_bytes + T * 16 * 3584 * 2
     up_gbs = up_bytes / up_us / 1e3
-    traffic = recorded_traffic(T, a.zipf)
+    traffic = recorded_traffic(T, a.zipf, a.row_major)
 
     res = {
         "metric": "MoE-layer decode tokens/s at 256 tokens; % of HBM roofline (GB/s achieved)",
@@ -192,12 +200,14 @@ def main():
         "data": "synthetic (seeded; random-init weights of the layer's shapes)",
         "config": {"workload": f"wide latent-MoE decode layer, T={T} tokens, hidden 7168, latent "
                                f"3584, 896 MXFP4 experts top-16, expert inter 512, shared inter "
-                               f"6144, {'Zipf' if a.zipf else 'uniform'} routing bias",
+                               f"6144, {'Zipf' if a.zipf else 'uniform'} routing bias, "
+                               f"{'row-major' if a.row_major else 'packed'} expert weights",
                    "tokens": T, "touched_experts": D, "units": nu},
         "layer_roofline": {"bound": "hbm", "weight_bytes": layer_bytes,
                            "achieved": layer_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": layer_gbs / HBM_PEAK_GBS},
-        "roofline": {"kernel": "k_ffn_up_fast (gate/up pass of the grouped expert FFN)",
+        "roofline": {"kernel": "k_ffn_up_fast (gate/up pass of the grouped expert FFN, "
+                               + ("row-major" if a.row_major else "packed") + " expert weights)",
                      "bound": "hbm", "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": up_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": up_bytes, "us_per_launch": up_us},

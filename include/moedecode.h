@@ -52,7 +52,9 @@ typedef enum {
 /* expert weight / activation format */
 enum { MOE_FMT_MXFP4_MXFP8 = 0, /* MXFP4 (E2M1 + E8M0 per 32) weights x MXFP8 (E4M3 + E8M0
                                    per 32) activations, MXFP8 hidden ([wide] precision) */
-       MOE_FMT_BF16 = 1 };      /* BF16 weights and activations (small test models) */
+       MOE_FMT_BF16 = 1,        /* BF16 weights and activations (small test models) */
+       MOE_FMT_MXFP4_MXFP8_PACKED = 2 }; /* the same arithmetic with the expert weights in
+                                   the packed layout of moe_pack_expert_weights */
 
 /* moe_router_topk flags */
 enum { MOE_LOGITS_GIVEN = 1 }; /* skip the router GEMM and read `logits` as input */
@@ -67,8 +69,8 @@ typedef struct {
 } moe_dims;
 
 /* One unit window: `count` (1..unit_tokens) consecutive entries pairs[begin ..] of one
-   expert's routing list ([wide] module summary: "every touched expert streams once per
-   8 of its tokens").  expert_total is the expert's whole list length on its first window
+   expert's routing list ([wide] module summary: the grouped engine's unit windows, one
+   pass over a touched expert's weights per 8 of its tokens).  expert_total is the expert's whole list length on its first window
    and 0 on its later windows (the grouped FFN streams an expert once for all of its
    windows). */
 typedef struct {
@@ -124,8 +126,8 @@ moe_status moe_build_lists(const moe_dims* d, const int32_t* ids, int32_t* count
                            int32_t* num_units, void* workspace, size_t ws_bytes, void* stream);
 size_t moe_lists_workspace_size(const moe_dims* d);
 
-/* MXFP8 quantisation of BF16 rows ([wide] module summary: the latent "written as the
-   experts' MXFP8 plan"; WideRoute's plan rows).  Per 32-element block: X =
+/* MXFP8 quantisation of BF16 rows ([wide] module summary: the latent row becomes the
+   experts' MXFP8 input; WideRoute's plan rows).  Per 32-element block: X =
    floor(log2 amax) - 8 clamped to [-127, 127], scale byte X + 127 (0 for an all-zero
    block), codes = E4M3 round-to-nearest-even of v / 2^X, saturating at +-448, zero
    sign kept.  codes [rows, cols] u8, scales [rows, cols/32] u8; cols % 32 == 0. */
@@ -149,6 +151,26 @@ moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const
                            const moe_unit* units, const int32_t* num_units, void* rows,
                            void* workspace, size_t ws_bytes, void* stream);
 size_t moe_ffn_workspace_size(const moe_dims* d);
+
+/* Load-time preparation of MXFP4 expert weights for the grouped FFN's loads (the pages
+   prepare weights ahead of the decode step too: [wide] WideMoE prepares the layer's
+   persistent experts for the wide batches, and [ep] pack_front packs the front GEMM's
+   weights).  src holds the row-major tensors described at
+   moe_expert_weights; dst receives the same bytes reordered, buffers of the same sizes,
+   for use with expert_format = MOE_FMT_MXFP4_MXFP8_PACKED:
+     W13 of expert e: 1 KiB blocks (j, w, m, i) for j < I/32, w < 4, m < 4, i < L/512; lane
+       l = r + 16 g of a block holds the 16 bytes of row (m / 2) I + 32 j + 16 (m % 2) + r,
+       K elements 32 (4 (L/512 w + i) + g) .. +31;
+     S13 of expert e: for (j, w, m, r) the L/512 scale dwords of that row starting at
+       byte 4 (L/512) w;
+     W2 of expert e: 1 KiB blocks (jd, w, m, s) for jd < L/512, w < 4, m < 8, s < I/128;
+       lane l = r + 16 g holds row 512 jd + 128 w + 16 m + r, K elements 32 (4 s + g) .. +31;
+     S2: unchanged.
+   The arithmetic of every call is unchanged; only the weight loads differ.  Requires
+   latent % 512 == 0 (latent <= 3584) and expert_inter / 128 in {1, 2, 4}; src and dst
+   must not overlap.  d->tokens is ignored beyond the dims check. */
+moe_status moe_pack_expert_weights(const moe_dims* d, const moe_expert_weights* src,
+                                   const moe_expert_weights* dst, void* stream);
 
 /* One pass of the grouped FFN above (MXFP4 x MXFP8 experts only), for callers that time
    or schedule the two expert passes apart.  stages = MOE_FFN_UP: steps (1)-(3) of the
@@ -178,8 +200,8 @@ moe_status moe_finalize(int32_t tokens, int32_t top_k, int32_t cols, const void*
 moe_status moe_rmsnorm(int32_t rows, int32_t cols, const void* r, const void* g, float eps,
                        void* out, void* stream);
 
-/* Dense BF16 linear out = x W^T with FP32 accumulation ([wide] precision: "BF16
-   linears"; [ep] stock_order).  x [M, K], W [N, K] BF16.  mode MOE_LINEAR_F32: out FP32
+/* Dense BF16 linear out = x W^T with FP32 accumulation ([wide] precision paragraph: the
+   dense projections are BF16; [ep] stock_order).  x [M, K], W [N, K] BF16.  mode MOE_LINEAR_F32: out FP32
    [M, N]; MOE_LINEAR_BF16: out BF16 = one rounding; MOE_LINEAR_ADD_BF16: out BF16 =
    BF16(FP32(add) + acc), add [M, N] BF16 (may alias out) -- the shared.addmm_ of [ep].
    K % 64 == 0, N % 8 == 0.  workspace >= moe_linear_workspace_size(M, N, K) bytes. */

@@ -18,7 +18,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_F
     MOE_ERR_LAUNCH = range(7)
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_ALIGN", "MOE_ERR_WORKSPACE",
                 "MOE_ERR_FORMAT", "MOE_ERR_LAUNCH"]
-MOE_FMT_MXFP4_MXFP8, MOE_FMT_BF16 = 0, 1
+MOE_FMT_MXFP4_MXFP8, MOE_FMT_BF16, MOE_FMT_MXFP4_MXFP8_PACKED = 0, 1, 2
 MOE_LOGITS_GIVEN = 1
 MOE_LINEAR_F32, MOE_LINEAR_BF16, MOE_LINEAR_ADD_BF16 = 0, 1, 2
 WORKSPACE_FIELDS = ["logits", "ids", "weights", "counts", "offsets", "pairs", "units", "num_units",
@@ -51,7 +51,7 @@ class moe_layer_weights(C.Structure):
 
 
 EXPORTS = ["moe_router_topk", "moe_router_workspace_size", "moe_build_lists",
-           "moe_lists_workspace_size", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_stages",
+           "moe_lists_workspace_size", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_stages", "moe_pack_expert_weights",
            "moe_ffn_workspace_size", "moe_finalize", "moe_rmsnorm", "moe_linear",
            "moe_linear_workspace_size", "moe_silu_mul", "moe_layer", "moe_workspace_size",
            "moe_workspace_layout", "moe_version"]
@@ -79,6 +79,8 @@ def lib():
             "moe_grouped_ffn_stages": (i32, [D, C.POINTER(moe_expert_weights), v, v, v, v, v, v, v,
                                              sz, i32, v]),
             "moe_ffn_workspace_size": (sz, [D]),
+            "moe_pack_expert_weights": (i32, [D, C.POINTER(moe_expert_weights),
+                                              C.POINTER(moe_expert_weights), v]),
             "moe_finalize": (i32, [i32, i32, i32, v, v, v, v, v]),
             "moe_rmsnorm": (i32, [i32, i32, v, v, f, v, v]),
             "moe_linear": (i32, [i32, i32, i32, v, v, v, v, i32, v, sz, v]),
@@ -211,6 +213,17 @@ def moe_grouped_ffn(d, w13, s13, w2, s2, act, act_scales, pairs, units, num_unit
 
 
 MOE_FFN_UP, MOE_FFN_DOWN = 1, 2
+
+
+def moe_pack_expert_weights(d, w13, s13, w2, s2, stream=None):
+    """The packed copies (w13, s13, w2, s2) of MXFP4 expert weights, for
+    expert_format = MOE_FMT_MXFP4_MXFP8_PACKED (new tensors of the same shapes)."""
+    out = [torch.empty_like(t) for t in (w13, s13, w2, s2)]
+    src = expert_weights(w13, s13, w2, s2)
+    dst = expert_weights(*out)
+    st = lib().moe_pack_expert_weights(C.byref(d), C.byref(src), C.byref(dst), _stream(stream))
+    _check("moe_pack_expert_weights", st)
+    return tuple(out)
 
 
 def moe_grouped_ffn_stages(d, w13, s13, w2, s2, act, act_scales, pairs, units, num_units, rows,

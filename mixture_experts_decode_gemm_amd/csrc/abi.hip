@@ -33,6 +33,11 @@ moe_status check_dims(const moe_dims* d) {
     if (!(d->rms_eps >= 0.0f)) return MOE_ERR_SHAPE;
     if (d->expert_format == MOE_FMT_MXFP4_MXFP8) {
         if (d->latent % 256 || d->expert_inter % 128) return MOE_ERR_SHAPE;
+    } else if (d->expert_format == MOE_FMT_MXFP4_MXFP8_PACKED) {
+        const int is = d->expert_inter / 128;
+        if (d->latent % 512 || d->latent > 3584 || d->expert_inter % 128 ||
+            (is != 1 && is != 2 && is != 4))
+            return MOE_ERR_SHAPE;
     } else if (d->expert_format == MOE_FMT_BF16) {
         if (d->expert_inter > 4096) return MOE_ERR_SHAPE;
     } else {
@@ -158,7 +163,8 @@ moe_status moe_grouped_ffn_stages(const moe_dims* d, const moe_expert_weights* w
     moe_status st = check_dims(d);
     if (st != MOE_OK) return st;
     if (stages < 1 || stages > 3) return MOE_ERR_FORMAT;
-    const bool mx = d->expert_format == MOE_FMT_MXFP4_MXFP8;
+    const bool packed = d->expert_format == MOE_FMT_MXFP4_MXFP8_PACKED;
+    const bool mx = d->expert_format == MOE_FMT_MXFP4_MXFP8 || packed;
     if (!mx && stages != 3) return MOE_ERR_FORMAT;
     const bool up = stages & MOE_FFN_UP, down = stages & MOE_FFN_DOWN;
     if (!w || !pairs || !units || !num_units) return MOE_ERR_NULL;
@@ -181,7 +187,7 @@ moe_status moe_grouped_ffn_stages(const moe_dims* d, const moe_expert_weights* w
             d->tokens, d->top_k, d->experts, d->latent, d->expert_inter, d->unit_tokens,
             (const uint8_t*)w->w13, (const uint8_t*)w->s13, (const uint8_t*)w->w2,
             (const uint8_t*)w->s2, (const uint8_t*)act, act_scales, pairs, (const int32_t*)units,
-            num_units, rows, hid, hsc, stages, s));
+            num_units, rows, hid, hsc, stages, packed, s));
     }
     return launch_status(launch_ffn_bf16(d->tokens, d->top_k, d->experts, d->latent,
                                          d->expert_inter, d->unit_tokens, w->w13, w->w2, act,
@@ -194,6 +200,26 @@ moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const
                            void* workspace, size_t ws_bytes, void* stream) {
     return moe_grouped_ffn_stages(d, w, act, act_scales, pairs, units, num_units, rows,
                                   workspace, ws_bytes, MOE_FFN_UP | MOE_FFN_DOWN, stream);
+}
+
+moe_status moe_pack_expert_weights(const moe_dims* d, const moe_expert_weights* src,
+                                   const moe_expert_weights* dst, void* stream) {
+    if (!d || !src || !dst) return MOE_ERR_NULL;
+    moe_dims pd = *d;
+    pd.expert_format = MOE_FMT_MXFP4_MXFP8_PACKED;
+    const moe_status st = check_dims(&pd);
+    if (st != MOE_OK) return st;
+    const void* ptrs[] = {src->w13, src->s13, src->w2, src->s2, dst->w13, dst->s13, dst->w2,
+                          dst->s2};
+    for (const void* p : ptrs) {
+        if (!p) return MOE_ERR_NULL;
+        if (!al16(p)) return MOE_ERR_ALIGN;
+    }
+    return launch_status(launch_pack_experts(
+        d->experts, d->latent, d->expert_inter, (const uint8_t*)src->w13,
+        (const uint8_t*)src->s13, (const uint8_t*)src->w2, (const uint8_t*)src->s2,
+        (uint8_t*)dst->w13, (uint8_t*)dst->s13, (uint8_t*)dst->w2, (uint8_t*)dst->s2,
+        (hipStream_t)stream));
 }
 
 moe_status moe_finalize(int32_t tokens, int32_t top_k, int32_t cols, const void* rows,
@@ -261,7 +287,8 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     if (!w->w_gate || !w->bias || !w->w_down || !w->w_shared_gu || !w->w_shared_down ||
         !w->norm_w || !w->w_up || !w->experts.w13 || !w->experts.w2)
         return MOE_ERR_NULL;
-    const bool mx = d->expert_format == MOE_FMT_MXFP4_MXFP8;
+    const bool packed = d->expert_format == MOE_FMT_MXFP4_MXFP8_PACKED;
+    const bool mx = d->expert_format == MOE_FMT_MXFP4_MXFP8 || packed;
     if (mx && (!w->experts.s13 || !w->experts.s2)) return MOE_ERR_NULL;
     const void* ptrs[] = {w->w_gate, w->bias, w->w_down, w->w_shared_gu, w->w_shared_down,
                           w->norm_w, w->w_up, w->experts.w13, w->experts.w2, x, out, workspace};
@@ -311,7 +338,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_ffn_mx(T, K, E, L, I, d->unit_tokens, (const uint8_t*)w->experts.w13,
                               (const uint8_t*)w->experts.s13, (const uint8_t*)w->experts.w2,
                               (const uint8_t*)w->experts.s2, codes, scales, pairs, units, nu,
-                              rows, hid, hid_scales, 3, s));
+                              rows, hid, hid_scales, 3, packed, s));
     } else {
         MOE_TRY(launch_ffn_bf16(T, K, E, L, I, d->unit_tokens, w->experts.w13, w->experts.w2,
                                 latent, pairs, units, nu, rows, s));

@@ -15,13 +15,15 @@
 // bytes 16-31.
 //
 // Two launches:
-//   up   -- item = (unit, 32 columns j of the expert intermediate).  Four wavefronts
-//           split the L/128 K-steps round-robin; each computes gate rows 32j..32j+31 and
-//           up rows I+32j..I+32j+31 (four 16-row tiles) for all tokens, partial sums are
-//           added across wavefronts in LDS in a fixed order, then silu(gate)*up in FP32
-//           and the 32-column block is quantised to MXFP8 (one E8M0 scale per token).
-//   down -- item = (unit, 256 rows of W2).  Each wavefront owns 64 rows (four tiles)
-//           over all I/128 K-steps; outputs are rounded to BF16 into the pairs' rows.
+//   up   -- item = (touched expert, 32 columns j of the expert intermediate).  The four
+//           wavefronts split the L/128 K-steps; each computes gate rows 32j..32j+31 and
+//           up rows I+32j..I+32j+31 (four 16-row tiles) for all of the expert's tokens,
+//           partial sums are added across wavefronts in LDS in a fixed order, then
+//           silu(gate)*up in FP32 and the 32-column block is quantised to MXFP8 (one E8M0
+//           scale per token).
+//   down -- item = (touched expert, 64*MT rows of W2).  Each wavefront owns 16*MT rows
+//           (MT tiles) over all I/128 K-steps; outputs are rounded to BF16 into the pairs'
+//           rows.
 // Both are persistent grid-stride loops over items; the item count comes from the
 // device-side unit count, so every workgroup reaches the same exit.
 #include "device.h"
@@ -74,7 +76,7 @@ __device__ __forceinline__ v8i as_fp4_operand(uint4 a) {
 // `pair` is the pair id of token n0 + (lane % 16) (valid where that token exists); it
 // is exchanged by lane shuffles, so the epilogue issues no global load (a load here
 // would have to wait behind every prefetch still in flight).
-__device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float (*red)[4][4][64],
+__device__ __forceinline__ void up_epilogue_lds(const v4f (&acc)[4], float (*red)[4][4][64],
                                             float (*hbuf)[17], int total, int n0, int pair,
                                             int j, int I, uint8_t* __restrict__ hid,
                                             uint8_t* __restrict__ hid_scales) {
@@ -118,21 +120,34 @@ __device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float (*red)[4]
     lds_barrier();
 }
 
+// dword loads at 4-byte alignment (scale bytes of one row, a wavefront's share)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
+template <int N>
+__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t (&out)[N]) {
+#pragma unroll
+    for (int k = 0; k + 4 <= N; k += 4) {
+        const u32x4 v = *(const u32x4_a4*)(p + 4 * k);
+        out[k] = v.x; out[k + 1] = v.y; out[k + 2] = v.z; out[k + 3] = v.w;
+    }
+#pragma unroll
+    for (int k = N & ~3; k < N; ++k) out[k] = *(const uint32_t*)(p + 4 * k);
+}
+
 // Up projection, latent L = 512 * SPW.  Item = (touched expert u < D, 32 columns j): the
-// expert's tile (gate rows 32j.., up rows I+32j.., 64 x L FP4, 114 KiB at L = 3584) is
+// expert's tile (gate rows 32j.., up rows I+32j.., 64 x L FP4, 112 KiB at L = 3584) is
 // streamed ONCE into registers -- wavefront w holds K steps SPW*w .. SPW*w+SPW-1 of the
-// four 16-row tiles -- and applied to all of the expert's tokens, 16 per MFMA column
-// tile.  One workgroup per CU runs a software pipeline: while item i is computed, the
-// weights (and then the first activations) of item i + gridDim are already in flight,
-// so every CU keeps about one tile of HBM reads outstanding.  The tile's E8M0 scales are
-// staged in LDS.
+// four 16-row tiles, with those steps' E8M0 scale bytes as dwords -- and applied to all
+// of the expert's tokens, 16 per MFMA column tile.  One workgroup per CU runs a software
+// pipeline: while item i is computed, the weights (and then the first activations) of
+// item i + gridDim are already in flight.
 template <int SPW>
 struct UpStage {
-    uint4 w[4][SPW];  // FP4 weight fragments
-    uint4 sc[2];      // this thread's share of the 64 x L/32 scale tile
-    v8i b[SPW];       // FP8 activation fragments of the current token group
-    int sb[SPW];      // their scale bytes
-    int4 un;          // (expert, list begin, window, list length)
+    uint4 w[4][SPW];        // FP4 weight fragments
+    uint32_t ws[4][SPW];    // their scale dwords (byte g = K block 4s+g)
+    v8i b[SPW];             // FP8 activation fragments of the current token group
+    uint32_t bs[SPW];       // their scale dwords
+    int4 un;                // (expert, list begin, window, list length)
     int j, pair;
 };
 
@@ -140,13 +155,13 @@ struct UpStage {
 // valid address and discard it) so that the same number of loads is outstanding on every
 // path: the compiler can then wait for exactly the current item's data (s_waitcnt
 // vmcnt(N)) and leave the next item's loads in flight.
-template <int SPW>
+template <int SPW, bool PACKED>
 __device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int nt, int I,
                                                  const uint8_t* __restrict__ w13,
                                                  const uint8_t* __restrict__ s13,
                                                  const int32_t* __restrict__ pairs,
                                                  const int4* __restrict__ units) {
-    constexpr int L = SPW * 512, SROW = L / 32, CH = SROW / 16;
+    constexpr int L = SPW * 512, SROW = L / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int u = item / nt;
@@ -156,25 +171,34 @@ __device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int
     // the first token group's pair ids, issued before the weights so that the
     // activation addresses can wait on them without waiting on the weights
     st.pair = pairs[st.un.y + min(r16, st.un.w - 1)];
-    const size_t ebase = (size_t)e * 2 * I;
+    if (PACKED) {
+        // packed layout: this wavefront's fragments are 4*SPW consecutive 1 KiB blocks
+        // (tile-major, then step), each in lane order; the scale dwords of tile m, row r16
+        // are SPW consecutive dwords
+        const size_t blk = (size_t)st.j * 4 + wave;
+        const uint8_t* wb = w13 + (size_t)e * I * L + blk * (4 * SPW * 1024) + lane * 16;
+        const uint8_t* sbase = s13 + (size_t)e * I * (L / 16) + blk * (4 * 16 * 4 * SPW);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = min((int)threadIdx.x + 256 * q, 64 * CH - 1);
-        const int row = c / CH, ch = c - row * CH, m = row >> 4;
-        const size_t R = ebase + (m >> 1) * I + st.j * UP_COLS + (m & 1) * 16 + (row & 15);
-        st.sc[q] = *(const uint4*)(s13 + R * SROW + ch * 16);
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) st.w[m][i] = *(const uint4*)(wb + (m * SPW + i) * 1024);
+            load_dwords<SPW>(sbase + (m * 16 + r16) * (4 * SPW), st.ws[m]);
+        }
+        return;
     }
+    const size_t ebase = (size_t)e * 2 * I;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const size_t R = ebase + (m >> 1) * I + st.j * UP_COLS + (m & 1) * 16 + r16;
         const uint8_t* base = w13 + R * (L / 2) + (SPW * wave) * 64 + 16 * g;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) st.w[m][i] = *(const uint4*)(base + i * 64);
+        load_dwords<SPW>(s13 + R * SROW + 4 * SPW * wave, st.ws[m]);
     }
 }
 
 template <int SPW>
-__device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int n0, int K,
+__device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int K,
                                               const uint8_t* __restrict__ codes,
                                               const uint8_t* __restrict__ scales) {
     constexpr int L = SPW * 512, SROW = L / 32;
@@ -184,35 +208,82 @@ __device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int n0, int K,
     // column n depends on B column n only, and such columns are never stored
     const int t = st.pair / K;
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int s = SPW * wave + i;
-        st.b[i] = load_fp8x32(codes + (size_t)t * L + s * 128, g);
-        st.sb[i] = scales[(size_t)t * SROW + 4 * s + g];
+    for (int i = 0; i < SPW; ++i)
+        st.b[i] = load_fp8x32(codes + (size_t)t * L + (SPW * wave + i) * 128, g);
+    load_dwords<SPW>(scales + (size_t)t * SROW + 4 * SPW * wave, st.bs);
+}
+
+// Partial H tiles of the four wavefronts (each summed over its quarter of K), one buffer:
+// [wave][tile][token][row] FP32, tiles padded to 272 floats so that the gate and up reads
+// of one token fall in different LDS banks.
+constexpr int RED_TILE = 16 * 16 + 16;
+constexpr int RED_FLOATS = 16 * RED_TILE;
+
+// Epilogue of one token group: the K-split partials meet in LDS (one barrier; the buffer
+// alternates between groups, so a wavefront that runs ahead writes the other buffer).
+// Thread t then owns token n = t / 16 and columns c, c+1 (c = 2 (t mod 16)) of the
+// 32-column block: the four partials are added in wavefront order, act = silu(gate) * up
+// in FP32, the block's amax is a max over the 16 lanes of that token (lane shuffles), and
+// the two E4M3 codes go out as one 16-bit store, the E8M0 scale from the lane holding c=0.
+__device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float* __restrict__ red,
+                                            int total, int n0, int pair, int j, int I,
+                                            uint8_t* __restrict__ hid,
+                                            uint8_t* __restrict__ hid_scales) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        *(v4f*)(red + (wave * 4 + m) * RED_TILE + r16 * 16 + 4 * g) = acc[m];
+    lds_barrier();
+    const int n = threadIdx.x >> 4, c = 2 * (threadIdx.x & 15);
+    const int mg = c >> 4, cr = c & 15;
+    float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float2 gv = *(const float2*)(red + (w * 4 + mg) * RED_TILE + n * 16 + cr);
+        const float2 uv = *(const float2*)(red + (w * 4 + mg + 2) * RED_TILE + n * 16 + cr);
+        if (w == 0) {
+            g0 = gv.x; g1 = gv.y; u0 = uv.x; u1 = uv.y;
+        } else {
+            g0 += gv.x; g1 += gv.y; u0 += uv.x; u1 += uv.y;
+        }
+    }
+    const float a0 = g0 / (1.0f + expf(-g0)) * u0;
+    const float a1 = g1 / (1.0f + expf(-g1)) * u1;
+    uint32_t m0 = __float_as_uint(a0) & 0x7FFFFFFFu, m1 = __float_as_uint(a1) & 0x7FFFFFFFu;
+    uint32_t mag = m0 > m1 ? m0 : m1;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)mag, off, 64);
+        mag = mag > o ? mag : o;
+    }
+    const int X = mx_block_exponent(mag);
+    const uint32_t q0 = e4m3_rne_sat(ldexpf(a0, -X)), q1 = e4m3_rne_sat(ldexpf(a1, -X));
+    const int p = __shfl(pair, n, 64);  // lane n of every wavefront holds token n's pair
+    if (n0 + n < total) {
+        *(uint16_t*)(hid + (size_t)p * I + j * UP_COLS + c) = (uint16_t)(q0 | (q1 << 8));
+        if (c == 0) hid_scales[(size_t)p * (I / 32) + j] = (uint8_t)(X + 127);
     }
 }
 
 template <int SPW>
 __device__ __forceinline__ void up_group(UpStage<SPW>& st, int n0, int I,
-                                         const int32_t* __restrict__ pairs,
-                                         uint8_t* __restrict__ hid, uint8_t* __restrict__ hid_scales,
-                                         const uint8_t* wsc, float (*red)[4][4][64],
-                                         float (*hbuf)[17]) {
-    constexpr int L = SPW * 512, SROW = L / 32;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, g = lane >> 4;
+                                         uint8_t* __restrict__ hid,
+                                         uint8_t* __restrict__ hid_scales, float* red) {
+    const int g = (threadIdx.x & 63) >> 4;
     v4f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+    // the MFMA reads its scales from bits 7:0 of the scale operands
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int s = SPW * wave + i;
+        const int sb = (int)(st.bs[i] >> (8 * g));
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int sa = wsc[(m * 16 + r16) * SROW + 4 * s + g];
-            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), st.b[i], acc[m], sa, st.sb[i]);
-        }
+        for (int m = 0; m < 4; ++m)
+            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), st.b[i], acc[m],
+                                  (int)(st.ws[m][i] >> (8 * g)), sb);
     }
-    up_epilogue(acc, red, hbuf, st.un.w, n0, st.pair, st.j, I, hid, hid_scales);
+    up_epilogue(acc, red, st.un.w, n0, st.pair, st.j, I, hid, hid_scales);
 }
 
 template <int SPW>
@@ -221,56 +292,49 @@ __device__ __forceinline__ void up_compute(UpStage<SPW>& st, int K, int I,
                                            const uint8_t* __restrict__ scales,
                                            const int32_t* __restrict__ pairs,
                                            uint8_t* __restrict__ hid,
-                                           uint8_t* __restrict__ hid_scales, uint8_t* wsc,
-                                           float (*red)[4][4][64], float (*hbuf)[17]) {
-    constexpr int L = SPW * 512, SROW = L / 32, CH = SROW / 16;
+                                           uint8_t* __restrict__ hid_scales, float* red,
+                                           int& rb) {
     const int r16 = threadIdx.x & 15;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = threadIdx.x + 256 * q;
-        if (c < 64 * CH) *(uint4*)(wsc + c * 16) = st.sc[q];
-    }
-    lds_barrier();
-    up_group(st, 0, I, pairs, hid, hid_scales, wsc, red, hbuf);
+    up_group(st, 0, I, hid, hid_scales, red + rb * RED_FLOATS);
+    rb ^= 1;
     for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later token groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
-        up_issue_acts(st, n0, K, codes, scales);
-        up_group(st, n0, I, pairs, hid, hid_scales, wsc, red, hbuf);
+        up_issue_acts(st, K, codes, scales);
+        up_group(st, n0, I, hid, hid_scales, red + rb * RED_FLOATS);
+        rb ^= 1;
     }
 }
 
-template <int SPW>
+template <int SPW, bool PACKED>
 __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int K, int I, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
     const int32_t* __restrict__ num_units, uint8_t* __restrict__ hid,
     uint8_t* __restrict__ hid_scales) {
-    constexpr int L = SPW * 512, SROW = L / 32;
-    __shared__ float red[4][4][4][64];
-    __shared__ float hbuf[64][17];
-    __shared__ __attribute__((aligned(16))) uint8_t wsc[64 * SROW];
+    __shared__ __attribute__((aligned(16))) float red[2 * RED_FLOATS];
     const int nt = I / UP_COLS;
     const int items = num_units[2] * nt;  // touched experts x column tiles
     const int G = gridDim.x;
     int item = blockIdx.x;
     if (item >= items) return;
+    int rb = 0;
     UpStage<SPW> A, B;
-    up_issue_weights(A, item, nt, I, w13, s13, pairs, units);
-    up_issue_acts(A, 0, K, codes, scales);
+    up_issue_weights<SPW, PACKED>(A, item, nt, I, w13, s13, pairs, units);
+    up_issue_acts(A, K, codes, scales);
     for (;;) {
         // the next item (or, past the end, this one again: a harmless repeat load)
         int nxt = item + G;
-        up_issue_weights(B, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
-        up_compute(A, K, I, codes, scales, pairs, hid, hid_scales, wsc, red, hbuf);
+        up_issue_weights<SPW, PACKED>(B, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
+        up_compute(A, K, I, codes, scales, pairs, hid, hid_scales, red, rb);
         if (nxt >= items) break;
-        up_issue_acts(B, 0, K, codes, scales);
+        up_issue_acts(B, K, codes, scales);
         item = nxt;
         nxt = item + G;
-        up_issue_weights(A, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
-        up_compute(B, K, I, codes, scales, pairs, hid, hid_scales, wsc, red, hbuf);
+        up_issue_weights<SPW, PACKED>(A, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
+        up_compute(B, K, I, codes, scales, pairs, hid, hid_scales, red, rb);
         if (nxt >= items) break;
-        up_issue_acts(A, 0, K, codes, scales);
+        up_issue_acts(A, K, codes, scales);
         item = nxt;
     }
 }
@@ -320,7 +384,7 @@ __global__ __launch_bounds__(256) void k_ffn_up_generic(
                     acc[m] = mfma_fp4_fp8(a, b, acc[m], sa, sb);
                 }
             }
-            up_epilogue(acc, red, hbuf, total, n0, pair, j, I, hid, hid_scales);
+            up_epilogue_lds(acc, red, hbuf, total, n0, pair, j, I, hid, hid_scales);
         }
     }
 }
@@ -333,14 +397,14 @@ __global__ __launch_bounds__(256) void k_ffn_up_generic(
 template <int IS, int MT>
 struct DownStage {
     uint4 w[MT][IS];
-    uint32_t sw[MT][IS];
+    uint32_t sw[MT][IS];  // scale dwords of each row (byte g = K block 4s+g)
     v8i b[IS];
-    int sb[IS];
+    uint32_t bs[IS];      // the hidden's scale dwords
     int4 un;
     int j, pair;
 };
 
-template <int IS, int MT>
+template <int IS, int MT, bool PACKED>
 __device__ __forceinline__ void down_issue_weights(DownStage<IS, MT>& st, int item, int nt, int L,
                                                    const uint8_t* __restrict__ w2,
                                                    const uint8_t* __restrict__ s2,
@@ -354,14 +418,18 @@ __device__ __forceinline__ void down_issue_weights(DownStage<IS, MT>& st, int it
     st.un = units[u];
     st.pair = pairs[st.un.y + min(r16, st.un.w - 1)];
     const size_t R0 = (size_t)st.un.x * L + st.j * (64 * MT) + wave * (16 * MT) + r16;
+    // packed layout: this wavefront's fragments are MT*IS consecutive 1 KiB blocks in
+    // lane order (the scale rows keep their order)
+    const uint8_t* wb = w2 + (size_t)st.un.x * L * WROW +
+                        ((size_t)st.j * 4 + wave) * (MT * IS * 1024) + lane * 16;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const size_t R = R0 + m * 16;
 #pragma unroll
-        for (int s = 0; s < IS; ++s) {
-            st.w[m][s] = *(const uint4*)(w2 + R * WROW + s * 64 + 16 * g);
-            st.sw[m][s] = *(const uint32_t*)(s2 + R * SROW + 4 * s);
-        }
+        for (int s = 0; s < IS; ++s)
+            st.w[m][s] = PACKED ? *(const uint4*)(wb + (m * IS + s) * 1024)
+                                : *(const uint4*)(w2 + R * WROW + s * 64 + 16 * g);
+        load_dwords<IS>(s2 + R * SROW, st.sw[m]);
     }
 }
 
@@ -374,10 +442,8 @@ __device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st,
     constexpr int I = IS * 128, SROW = I / 32;
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-    for (int s = 0; s < IS; ++s) {
-        st.b[s] = load_fp8x32(hid + (size_t)st.pair * I + s * 128, g);
-        st.sb[s] = hid_scales[(size_t)st.pair * SROW + 4 * s + g];
-    }
+    for (int s = 0; s < IS; ++s) st.b[s] = load_fp8x32(hid + (size_t)st.pair * I + s * 128, g);
+    load_dwords<IS>(hid_scales + (size_t)st.pair * SROW, st.bs);
 }
 
 template <int IS, int MT>
@@ -393,7 +459,7 @@ __device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L,
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][s]), st.b[s], acc[m],
-                                  (int)((st.sw[m][s] >> (8 * g)) & 0xFFu), st.sb[s]);
+                                  (int)(st.sw[m][s] >> (8 * g)), (int)(st.bs[s] >> (8 * g)));
     if (n0 + r16 < st.un.w) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -421,7 +487,7 @@ __device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L,
     }
 }
 
-template <int IS, int MT>
+template <int IS, int MT, bool PACKED>
 __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     int L, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
     const uint8_t* __restrict__ hid, const uint8_t* __restrict__ hid_scales,
@@ -433,17 +499,17 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     int item = blockIdx.x;
     if (item >= items) return;
     DownStage<IS, MT> A, B;
-    down_issue_weights(A, item, nt, L, w2, s2, pairs, units);
+    down_issue_weights<IS, MT, PACKED>(A, item, nt, L, w2, s2, pairs, units);
     down_issue_acts(A, hid, hid_scales);
     for (;;) {
         int nxt = item + G;
-        down_issue_weights(B, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
+        down_issue_weights<IS, MT, PACKED>(B, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
         down_compute(A, L, hid, hid_scales, pairs, rows);
         if (nxt >= items) break;
         down_issue_acts(B, hid, hid_scales);
         item = nxt;
         nxt = item + G;
-        down_issue_weights(A, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
+        down_issue_weights<IS, MT, PACKED>(A, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
         down_compute(B, L, hid, hid_scales, pairs, rows);
         if (nxt >= items) break;
         down_issue_acts(A, hid, hid_scales);
@@ -528,18 +594,25 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const uint8_t* s13, const uint8_t* w2, const uint8_t* s2,
                          const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
                          const int32_t* units, const int32_t* num_units, void* rows,
-                         uint8_t* hid, uint8_t* hsc, int stages, hipStream_t s) {
+                         uint8_t* hid, uint8_t* hsc, int stages, bool packed, hipStream_t s) {
     (void)T;
     (void)unit;
     const int4* un = (const int4*)units;
     const int up_items = E * (I / UP_COLS);  // an upper bound: the kernels read D on the device
     const int cus = num_cus();
     const dim3 blk(256);
+    const dim3 ugrid(up_items < cus ? up_items : cus);
+    // packed weights exist only for L % 512 == 0 and I / 128 in {1, 2, 4} (checked by the
+    // callers), which the fast kernels cover
     switch ((stages & 1) ? (L % 512 == 0 ? L / 512 : 0) : -1) {
 #define MOE_UP(SPW)                                                                          \
     case SPW:                                                                                \
-        hipLaunchKernelGGL(k_ffn_up_fast<SPW>, dim3(up_items < cus ? up_items : cus), blk, 0, \
-                           s, K, I, w13, s13, codes, scales, pairs, un, num_units, hid, hsc);  \
+        if (packed)                                                                          \
+            hipLaunchKernelGGL((k_ffn_up_fast<SPW, true>), ugrid, blk, 0, s, K, I, w13, s13, \
+                               codes, scales, pairs, un, num_units, hid, hsc);               \
+        else                                                                                 \
+            hipLaunchKernelGGL((k_ffn_up_fast<SPW, false>), ugrid, blk, 0, s, K, I, w13, s13,\
+                               codes, scales, pairs, un, num_units, hid, hsc);               \
         break;
         MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7)
 #undef MOE_UP
@@ -551,12 +624,16 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     }
     const int MTsel = L % 512 == 0 ? 8 : (L % 256 == 0 ? 4 : 0);
     const int down_items = MTsel ? E * (L / (64 * MTsel)) : E * (L / DOWN_ROWS);
-    const int dgrid = down_items < cus ? down_items : cus;
+    const dim3 dgrid(down_items < cus ? down_items : cus);
     switch ((stages & 2) ? MTsel * 10 + I / 128 : -1) {
 #define MOE_DOWN(MT, IS)                                                                     \
     case MT * 10 + IS:                                                                       \
-        hipLaunchKernelGGL((k_ffn_down_fast<IS, MT>), dim3(dgrid), blk, 0, s, L, w2, s2, hid,  \
-                           hsc, pairs, un, num_units, (uint16_t*)rows);                      \
+        if (packed && MT == 8)                                                               \
+            hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, true>), dgrid, blk, 0, s, L, w2, s2, \
+                               hid, hsc, pairs, un, num_units, (uint16_t*)rows);             \
+        else                                                                                 \
+            hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, false>), dgrid, blk, 0, s, L, w2, s2,\
+                               hid, hsc, pairs, un, num_units, (uint16_t*)rows);             \
         break;
         MOE_DOWN(8, 1) MOE_DOWN(8, 2) MOE_DOWN(8, 4) MOE_DOWN(4, 1) MOE_DOWN(4, 2)
         MOE_DOWN(4, 4)
@@ -567,6 +644,90 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
             hipLaunchKernelGGL(k_ffn_down_generic, dim3(persistent_blocks(down_items, 8)), blk, 0,
                                s, L, I, w2, s2, hid, hsc, pairs, un, num_units, (uint16_t*)rows);
     }
+    return hipGetLastError();
+}
+
+// ---- the packed expert layout (load-time preparation of MXFP4 weights) -----------------
+// W13 of expert e: blocks (j, w, m, i) of 1 KiB, j < I/32 the 32-column item, w < 4 the
+// wavefront, m < 4 the 16-row tile (gate 0-15, gate 16-31, up 0-15, up 16-31 of the item's
+// columns), i < L/512 the wavefront's K step; lane l = r + 16 g of a block holds the 16
+// bytes of row r of tile m, K block g of step L/512*w + i.  S13 of expert e: for (j, w, m, r)
+// the L/512 scale dwords of that row covering the wavefront's steps.  W2 of expert e:
+// blocks (jd, w, m, s), jd < L/512 the 512-row item, w < 4, m < 8 the 16-row tile (rows
+// 512 jd + 128 w + 16 m ..), s < I/128 the K step, lanes as above.  S2 is unchanged.
+__global__ __launch_bounds__(256) void k_pack_w13(long total, int I, int L,
+                                                  const uint4* __restrict__ src,
+                                                  uint4* __restrict__ dst) {
+    const int SPW = L / 512;
+    const long per_e = (long)I * L / 16;
+    for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < total; c += (long)gridDim.x * 256) {
+        const long e = c / per_e;
+        long r = c - e * per_e;
+        const int lane = (int)(r % 64); r /= 64;
+        const int i = (int)(r % SPW); r /= SPW;
+        const int m = (int)(r % 4); r /= 4;
+        const int w = (int)(r % 4);
+        const int j = (int)(r / 4);
+        const long row = (long)(m >> 1) * I + j * UP_COLS + (m & 1) * 16 + (lane & 15);
+        const long col16 = (long)(SPW * w + i) * 4 + (lane >> 4);  // 16-byte unit in the row
+        dst[c] = src[e * per_e + row * (L / 32) + col16];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_pack_s13(long total, int I, int L,
+                                                  const uint32_t* __restrict__ src,
+                                                  uint32_t* __restrict__ dst) {
+    const int SPW = L / 512;
+    const long per_e = (long)I * L / 64;  // dwords per expert
+    for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < total; c += (long)gridDim.x * 256) {
+        const long e = c / per_e;
+        long r = c - e * per_e;
+        const int k = (int)(r % SPW); r /= SPW;
+        const int r16 = (int)(r % 16); r /= 16;
+        const int m = (int)(r % 4); r /= 4;
+        const int w = (int)(r % 4);
+        const int j = (int)(r / 4);
+        const long row = (long)(m >> 1) * I + j * UP_COLS + (m & 1) * 16 + r16;
+        dst[c] = src[e * per_e + row * (L / 128) + SPW * w + k];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_pack_w2(long total, int I, int L,
+                                                 const uint4* __restrict__ src,
+                                                 uint4* __restrict__ dst) {
+    const int IS = I / 128;
+    const long per_e = (long)I * L / 32;
+    for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < total; c += (long)gridDim.x * 256) {
+        const long e = c / per_e;
+        long r = c - e * per_e;
+        const int lane = (int)(r % 64); r /= 64;
+        const int s = (int)(r % IS); r /= IS;
+        const int m = (int)(r % 8); r /= 8;
+        const int w = (int)(r % 4);
+        const int jd = (int)(r / 4);
+        const long row = (long)jd * 512 + w * 128 + m * 16 + (lane & 15);
+        dst[c] = src[e * per_e + row * (I / 32) + s * 4 + (lane >> 4)];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_copy_u32(long total, const uint32_t* __restrict__ src,
+                                                  uint32_t* __restrict__ dst) {
+    for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < total; c += (long)gridDim.x * 256)
+        dst[c] = src[c];
+}
+
+hipError_t launch_pack_experts(int E, int L, int I, const uint8_t* w13, const uint8_t* s13,
+                               const uint8_t* w2, const uint8_t* s2, uint8_t* pw13, uint8_t* ps13,
+                               uint8_t* pw2, uint8_t* ps2, hipStream_t s) {
+    const dim3 blk(256), grid(8 * num_cus());
+    hipLaunchKernelGGL(k_pack_w13, grid, blk, 0, s, (long)E * I * L / 16, I, L,
+                       (const uint4*)w13, (uint4*)pw13);
+    hipLaunchKernelGGL(k_pack_s13, grid, blk, 0, s, (long)E * I * L / 64, I, L,
+                       (const uint32_t*)s13, (uint32_t*)ps13);
+    hipLaunchKernelGGL(k_pack_w2, grid, blk, 0, s, (long)E * I * L / 32, I, L,
+                       (const uint4*)w2, (uint4*)pw2);
+    hipLaunchKernelGGL(k_copy_u32, grid, blk, 0, s, (long)E * I * L / 128, (const uint32_t*)s2,
+                       (uint32_t*)ps2);
     return hipGetLastError();
 }
 

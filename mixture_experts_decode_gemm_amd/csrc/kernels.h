@@ -31,7 +31,12 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const uint8_t* s13, const uint8_t* w2, const uint8_t* s2,
                          const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
                          const int32_t* units, const int32_t* num_units, void* rows,
-                         uint8_t* hid, uint8_t* hid_scales, int stages, hipStream_t s);
+                         uint8_t* hid, uint8_t* hid_scales, int stages, bool packed,
+                         hipStream_t s);
+// the packed expert layout (see ffn.hip); L % 512 == 0, I / 128 in {1, 2, 4}
+hipError_t launch_pack_experts(int E, int L, int I, const uint8_t* w13, const uint8_t* s13,
+                               const uint8_t* w2, const uint8_t* s2, uint8_t* pw13, uint8_t* ps13,
+                               uint8_t* pw2, uint8_t* ps2, hipStream_t s);
 hipError_t launch_ffn_bf16(int T, int K, int E, int L, int I, int unit, const void* w13,
                            const void* w2, const void* latent, const int32_t* pairs,
                            const int32_t* units, const int32_t* num_units, void* rows,

@@ -139,6 +139,22 @@ def test_lists_and_ffn_reject(L):
                                     None) == moe.MOE_ERR_FORMAT
 
 
+def test_packed_format_and_pack_reject(L):
+    d = good_dims()
+    d.expert_format = moe.MOE_FMT_MXFP4_MXFP8_PACKED
+    assert moe.moe_workspace_size(d) > 0  # latent 3584, inter 512: accepted
+    w = moe.moe_expert_weights(FAKE, FAKE, FAKE, FAKE)
+    for latent, inter in ((3584 - 256, 512), (3584, 384), (4096, 512)):
+        d.latent, d.expert_inter = latent, inter
+        assert moe.moe_workspace_size(d) == 0
+        assert L.moe_pack_expert_weights(C.byref(d), C.byref(w), C.byref(w),
+                                         None) == moe.MOE_ERR_SHAPE
+    d = good_dims()
+    bad = moe.moe_expert_weights(FAKE, None, FAKE, FAKE)
+    assert L.moe_pack_expert_weights(C.byref(d), C.byref(w), C.byref(bad), None) == moe.MOE_ERR_NULL
+    assert L.moe_pack_expert_weights(None, C.byref(w), C.byref(w), None) == moe.MOE_ERR_NULL
+
+
 def test_linear_rmsnorm_silu_reject(L):
     assert L.moe_linear(8, 64, 100, FAKE, FAKE, FAKE, None, 1, None, 0, None) == moe.MOE_ERR_SHAPE
     assert L.moe_linear(8, 64, 128, FAKE, FAKE, FAKE, None, 5, None, 0, None) == moe.MOE_ERR_FORMAT

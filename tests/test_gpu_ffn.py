@@ -117,6 +117,82 @@ def test_ffn_stages_match_grouped():
     assert np.array_equal(host(rows), ref_rows)
 
 
+def pack_host(w13, s13, w2, s2, L, I):
+    """The packed layout of moe_pack_expert_weights, written out from its definition."""
+    E, SPW, IS = w13.shape[0], L // 512, I // 128
+    pw13 = np.empty_like(w13).reshape(E, -1)
+    ps13 = np.empty_like(s13).reshape(E, -1)
+    pw2 = np.empty_like(w2).reshape(E, -1)
+    for e in range(E):
+        o = 0
+        for j in range(I // 32):
+            for w in range(4):
+                for m in range(4):
+                    for i in range(SPW):
+                        for lane in range(64):
+                            r, g = lane % 16, lane // 16
+                            row = (m // 2) * I + 32 * j + 16 * (m % 2) + r
+                            k0 = (4 * (SPW * w + i) + g) * 16  # byte offset of K block
+                            pw13[e, o:o + 16] = w13[e, row, k0:k0 + 16]
+                            o += 16
+        o = 0
+        for j in range(I // 32):
+            for w in range(4):
+                for m in range(4):
+                    for r in range(16):
+                        row = (m // 2) * I + 32 * j + 16 * (m % 2) + r
+                        ps13[e, o:o + 4 * SPW] = s13[e, row, 4 * SPW * w:4 * SPW * (w + 1)]
+                        o += 4 * SPW
+        o = 0
+        for jd in range(L // 512):
+            for w in range(4):
+                for m in range(8):
+                    for st in range(IS):
+                        for lane in range(64):
+                            r, g = lane % 16, lane // 16
+                            row = 512 * jd + 128 * w + 16 * m + r
+                            k0 = (4 * st + g) * 16
+                            pw2[e, o:o + 16] = w2[e, row, k0:k0 + 16]
+                            o += 16
+    return pw13.reshape(w13.shape), ps13.reshape(s13.shape), pw2.reshape(w2.shape), s2.copy()
+
+
+def test_pack_layout_matches_definition():
+    """moe_pack_expert_weights against the layout its header states, built on the host."""
+    E, L, I = 2, 1024, 256
+    w = syn.expert_weights(dict(L=L, I=I, E=E, expert_format=0), seed=4)
+    d = moe.dims(8, 8, hidden=256, latent=L, experts=E, top_k=2, expert_inter=I)
+    got = moe.moe_pack_expert_weights(d, dev(w["w13"]), dev(w["s13"]), dev(w["w2"]), dev(w["s2"]))
+    torch.cuda.synchronize()
+    ref = pack_host(w["w13"], w["s13"], w["w2"], w["s2"], L, I)
+    for name, g_, r_ in zip(("w13", "s13", "w2", "s2"), got, ref):
+        assert np.array_equal(host(g_), r_), name
+
+
+@pytest.mark.parametrize("T,K,E,L,I,hot", [(16, 4, 8, 512, 128, None), (40, 4, 12, 1024, 256, 3),
+                                           (256, 16, 64, 3584, 512, 3)])
+def test_ffn_packed_equals_row_major(T, K, E, L, I, hot):
+    """The packed-weight FFN computes the same MFMAs on the same operands: rows and
+    hidden bit for bit equal to the row-major run (hot: an expert in every token)."""
+    say(f"ffn packed T={T} K={K} E={E} L={L} I={I}")
+    w = syn.expert_weights(dict(L=L, I=I, E=E, expert_format=0), seed=5)
+    codes, scales = syn.mxfp8_random(syn.rng(5, 703), T, L)
+    ids = random_ids(np.random.default_rng(T + 1), T, K, E, hot=hot)
+    d = moe.dims(T, T, hidden=256, latent=L, experts=E, top_k=K, expert_inter=I)
+    ref_rows, ref_hid, ref_hsc = run_ffn_mx(d, w, codes, scales, ids)
+    pk = moe.moe_pack_expert_weights(d, dev(w["w13"]), dev(w["s13"]), dev(w["w2"]), dev(w["s2"]))
+    dp = moe.dims(T, T, hidden=256, latent=L, experts=E, top_k=K, expert_inter=I,
+                  expert_format=moe.MOE_FMT_MXFP4_MXFP8_PACKED)
+    pairs, units, nu = build_lists(dp, dev(ids))
+    rows = torch.zeros(T * K, L, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(moe.moe_ffn_workspace_size(dp), dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_ffn(dp, *pk, dev(codes), dev(scales), pairs, units, nu, rows, ws)
+    torch.cuda.synchronize()
+    P = T * K
+    assert np.array_equal(host(ws[:P * I]).reshape(P, I), ref_hid)
+    assert np.array_equal(host(rows), ref_rows)
+
+
 def test_ffn_bf16_toy(orc):
     d0 = dict(syn.TOY)
     T, K, E, L, I = d0["T"], d0["K"], d0["E"], d0["L"], d0["I"]

@@ -99,3 +99,17 @@ def test_full_layer_teacher_forced(orc, T, zipf):
     d1 = dict(d0, T=len(sub))
     ref = orc.layer(d1, w, x[sub])
     assert_close(f32(out[sub]), f32(ref), "out (free-running oracle, sanity)", tol=0.1)
+
+
+def test_full_layer_packed_equals_row_major():
+    """moe_layer on packed expert weights gives the row-major layer's output bit for bit."""
+    w, dw = full_weights(0, False)
+    T = 256
+    x = syn.layer_input(syn.full_dims(T), seed=1)
+    d = moe.dims(T, T)
+    out_ref, _ = run_layer(d, dw, x)
+    pk = moe.moe_pack_expert_weights(d, dw["w13"], dw["s13"], dw["w2"], dw["s2"])
+    dwp = dict(dw, w13=pk[0], s13=pk[1], w2=pk[2], s2=pk[3])
+    dp = moe.dims(T, T, expert_format=moe.MOE_FMT_MXFP4_MXFP8_PACKED)
+    out, _ = run_layer(dp, dwp, x)
+    assert np.array_equal(out, out_ref)

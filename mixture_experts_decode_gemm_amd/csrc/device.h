@@ -74,6 +74,28 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier for code that also has direct global-to-LDS loads in flight: waits
+// for this wavefront's own LDS reads and writes (lgkmcnt) and nothing else.  A release
+// fence (lds_barrier) would make the compiler wait for every outstanding direct load
+// (they write LDS), draining a prefetch; here completion of direct loads is the caller's
+// business (wait_vmcnt before the barrier).  The asm statement is also a compiler-level
+// memory barrier, so no memory access moves across it.
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt and lgkmcnt left at their maxima).  Direct global-to-LDS loads are not
+// tracked by the compiler's own waits: code that reads what they wrote waits with this,
+// then crosses an LDS barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 // ---- wave helpers ---------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -24,8 +24,10 @@
 //   down -- item = (touched expert, 64*MT rows of W2).  Each wavefront owns 16*MT rows
 //           (MT tiles) over all I/128 K-steps; outputs are rounded to BF16 into the pairs'
 //           rows.
-// Both are persistent grid-stride loops over items; the item count comes from the
-// device-side unit count, so every workgroup reaches the same exit.
+// Both are persistent grid-stride loops over items (items i, i + G, i + 2G, ... of a
+// workgroup, so that at any time the CUs read one compact window of expert weights); the
+// item count comes from the device-side unit count, so every workgroup reaches the same
+// exit.
 #include "device.h"
 #include "kernels.h"
 
@@ -120,9 +122,14 @@ __device__ __forceinline__ void up_epilogue_lds(const v4f (&acc)[4], float (*red
     lds_barrier();
 }
 
-// dword loads at 4-byte alignment (scale bytes of one row, a wavefront's share)
+// dword loads at 4-byte alignment (scale bytes of one row, a wavefront's share): one
+// dwordx4 per 4 dwords and one x3/x2/x1 load for the rest
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
+typedef u32x3 __attribute__((aligned(4))) u32x3_a4;
+typedef u32x2 __attribute__((aligned(4))) u32x2_a4;
 template <int N>
 __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t (&out)[N]) {
 #pragma unroll
@@ -130,8 +137,16 @@ __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t (&out)[N]
         const u32x4 v = *(const u32x4_a4*)(p + 4 * k);
         out[k] = v.x; out[k + 1] = v.y; out[k + 2] = v.z; out[k + 3] = v.w;
     }
-#pragma unroll
-    for (int k = N & ~3; k < N; ++k) out[k] = *(const uint32_t*)(p + 4 * k);
+    constexpr int k = N & ~3;
+    if (N % 4 == 3) {
+        const u32x3 v = *(const u32x3_a4*)(p + 4 * k);
+        out[k] = v.x; out[k + 1 < N ? k + 1 : 0] = v.y; out[k + 2 < N ? k + 2 : 0] = v.z;
+    } else if (N % 4 == 2) {
+        const u32x2 v = *(const u32x2_a4*)(p + 4 * k);
+        out[k] = v.x; out[k + 1 < N ? k + 1 : 0] = v.y;
+    } else if (N % 4 == 1) {
+        out[k < N ? k : 0] = *(const uint32_t*)(p + 4 * k);
+    }
 }
 
 // Up projection, latent L = 512 * SPW.  Item = (touched expert u < D, 32 columns j): the
@@ -226,7 +241,7 @@ constexpr int RED_FLOATS = 16 * RED_TILE;
 // in FP32, the block's amax is a max over the 16 lanes of that token (lane shuffles), and
 // the two E4M3 codes go out as one 16-bit store, the E8M0 scale from the lane holding c=0.
 __device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float* __restrict__ red,
-                                            int total, int n0, int pair, int j, int I,
+                                            bool store, int total, int n0, int pair, int j, int I,
                                             uint8_t* __restrict__ hid,
                                             uint8_t* __restrict__ hid_scales) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -260,14 +275,14 @@ __device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float* __restri
     const int X = mx_block_exponent(mag);
     const uint32_t q0 = e4m3_rne_sat(ldexpf(a0, -X)), q1 = e4m3_rne_sat(ldexpf(a1, -X));
     const int p = __shfl(pair, n, 64);  // lane n of every wavefront holds token n's pair
-    if (n0 + n < total) {
+    if (store && n0 + n < total) {
         *(uint16_t*)(hid + (size_t)p * I + j * UP_COLS + c) = (uint16_t)(q0 | (q1 << 8));
         if (c == 0) hid_scales[(size_t)p * (I / 32) + j] = (uint8_t)(X + 127);
     }
 }
 
 template <int SPW>
-__device__ __forceinline__ void up_group(UpStage<SPW>& st, int n0, int I,
+__device__ __forceinline__ void up_group(UpStage<SPW>& st, int n0, int I, bool store,
                                          uint8_t* __restrict__ hid,
                                          uint8_t* __restrict__ hid_scales, float* red) {
     const int g = (threadIdx.x & 63) >> 4;
@@ -283,11 +298,11 @@ __device__ __forceinline__ void up_group(UpStage<SPW>& st, int n0, int I,
             acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), st.b[i], acc[m],
                                   (int)(st.ws[m][i] >> (8 * g)), sb);
     }
-    up_epilogue(acc, red, st.un.w, n0, st.pair, st.j, I, hid, hid_scales);
+    up_epilogue(acc, red, store, st.un.w, n0, st.pair, st.j, I, hid, hid_scales);
 }
 
 template <int SPW>
-__device__ __forceinline__ void up_compute(UpStage<SPW>& st, int K, int I,
+__device__ __forceinline__ void up_compute(UpStage<SPW>& st, int K, int I, bool store,
                                            const uint8_t* __restrict__ codes,
                                            const uint8_t* __restrict__ scales,
                                            const int32_t* __restrict__ pairs,
@@ -295,12 +310,12 @@ __device__ __forceinline__ void up_compute(UpStage<SPW>& st, int K, int I,
                                            uint8_t* __restrict__ hid_scales, float* red,
                                            int& rb) {
     const int r16 = threadIdx.x & 15;
-    up_group(st, 0, I, hid, hid_scales, red + rb * RED_FLOATS);
+    up_group(st, 0, I, store, hid, hid_scales, red + rb * RED_FLOATS);
     rb ^= 1;
     for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later token groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
         up_issue_acts(st, K, codes, scales);
-        up_group(st, n0, I, hid, hid_scales, red + rb * RED_FLOATS);
+        up_group(st, n0, I, store, hid, hid_scales, red + rb * RED_FLOATS);
         rb ^= 1;
     }
 }
@@ -322,20 +337,23 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     UpStage<SPW> A, B;
     up_issue_weights<SPW, PACKED>(A, item, nt, I, w13, s13, pairs, units);
     up_issue_acts(A, K, codes, scales);
-    for (;;) {
-        // the next item (or, past the end, this one again: a harmless repeat load)
-        int nxt = item + G;
-        up_issue_weights<SPW, PACKED>(B, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
-        up_compute(A, K, I, codes, scales, pairs, hid, hid_scales, red, rb);
-        if (nxt >= items) break;
+    // Items in pairs (A = item, B = item + G).  Nothing between a stage's loads and its
+    // compute is conditional: a conditional exit there would let the compiler sink the
+    // loads below it, losing the prefetch.  Past the last item a stage repeats an item,
+    // computes it and stores nothing.
+    for (; item < items; item += 2 * G) {
+        const bool b_real = item + G < items;
+        // (the scheduling barriers keep each stage's loads ahead of the other stage's
+        // compute; otherwise the scheduler interleaves them into it)
+        up_issue_weights<SPW, PACKED>(B, b_real ? item + G : item, nt, I, w13, s13, pairs, units);
+        __builtin_amdgcn_sched_barrier(0);
+        up_compute(A, K, I, true, codes, scales, pairs, hid, hid_scales, red, rb);
         up_issue_acts(B, K, codes, scales);
-        item = nxt;
-        nxt = item + G;
-        up_issue_weights<SPW, PACKED>(A, nxt < items ? nxt : item, nt, I, w13, s13, pairs, units);
-        up_compute(B, K, I, codes, scales, pairs, hid, hid_scales, red, rb);
-        if (nxt >= items) break;
+        const int na = item + 2 * G < items ? item + 2 * G : item;
+        up_issue_weights<SPW, PACKED>(A, na, nt, I, w13, s13, pairs, units);
+        __builtin_amdgcn_sched_barrier(0);
+        up_compute(B, K, I, b_real, codes, scales, pairs, hid, hid_scales, red, rb);
         up_issue_acts(A, K, codes, scales);
-        item = nxt;
     }
 }
 
@@ -447,7 +465,7 @@ __device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st,
 }
 
 template <int IS, int MT>
-__device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L,
+__device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L, bool store,
                                            uint16_t* __restrict__ rows) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -460,7 +478,7 @@ __device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L,
         for (int m = 0; m < MT; ++m)
             acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][s]), st.b[s], acc[m],
                                   (int)(st.sw[m][s] >> (8 * g)), (int)(st.bs[s] >> (8 * g)));
-    if (n0 + r16 < st.un.w) {
+    if (store && n0 + r16 < st.un.w) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int row = st.j * (64 * MT) + wave * (16 * MT) + m * 16 + 4 * g;
@@ -473,17 +491,17 @@ __device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L,
 }
 
 template <int IS, int MT>
-__device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L,
+__device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L, bool store,
                                              const uint8_t* __restrict__ hid,
                                              const uint8_t* __restrict__ hid_scales,
                                              const int32_t* __restrict__ pairs,
                                              uint16_t* __restrict__ rows) {
     const int r16 = threadIdx.x & 15;
-    down_group(st, 0, L, rows);
+    down_group(st, 0, L, store, rows);
     for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later pair groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
         down_issue_acts(st, hid, hid_scales);
-        down_group(st, n0, L, rows);
+        down_group(st, n0, L, store, rows);
     }
 }
 
@@ -501,19 +519,20 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     DownStage<IS, MT> A, B;
     down_issue_weights<IS, MT, PACKED>(A, item, nt, L, w2, s2, pairs, units);
     down_issue_acts(A, hid, hid_scales);
-    for (;;) {
-        int nxt = item + G;
-        down_issue_weights<IS, MT, PACKED>(B, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
-        down_compute(A, L, hid, hid_scales, pairs, rows);
-        if (nxt >= items) break;
+    // items in pairs, nothing conditional between a stage's loads and its compute (see
+    // the up projection)
+    for (; item < items; item += 2 * G) {
+        const bool b_real = item + G < items;
+        down_issue_weights<IS, MT, PACKED>(B, b_real ? item + G : item, nt, L, w2, s2, pairs,
+                                           units);
+        __builtin_amdgcn_sched_barrier(0);
+        down_compute(A, L, true, hid, hid_scales, pairs, rows);
         down_issue_acts(B, hid, hid_scales);
-        item = nxt;
-        nxt = item + G;
-        down_issue_weights<IS, MT, PACKED>(A, nxt < items ? nxt : item, nt, L, w2, s2, pairs, units);
-        down_compute(B, L, hid, hid_scales, pairs, rows);
-        if (nxt >= items) break;
+        const int na = item + 2 * G < items ? item + 2 * G : item;
+        down_issue_weights<IS, MT, PACKED>(A, na, nt, L, w2, s2, pairs, units);
+        __builtin_amdgcn_sched_barrier(0);
+        down_compute(B, L, b_real, hid, hid_scales, pairs, rows);
         down_issue_acts(A, hid, hid_scales);
-        item = nxt;
     }
 }
 

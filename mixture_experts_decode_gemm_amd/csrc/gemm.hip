@@ -80,16 +80,6 @@ __device__ __forceinline__ void store_out(void* out, const void* add, size_t idx
     }
 }
 
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
 // MODE: 0 FP32 out, 1 BF16 out, 2 BF16 out + add; 3 FP32 split partial (out = scratch)
 template <int MODE, int NS>
 __global__ __launch_bounds__(256) void k_gemm(int M, int N, int K, int kchunk,

@@ -16,9 +16,13 @@
  *     last dimension contiguous; BF16 is IEEE bfloat16 bits; every pointer to a tensor
  *     must be 16-byte aligned (MOE_ERR_ALIGN otherwise).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call
- *     only enqueues work: it never allocates, frees or synchronises, and keeps no
- *     state between calls (re-entrant; concurrent calls on different streams must not
- *     share output or workspace buffers).
+ *     only enqueues work: it never allocates device memory, frees or synchronises
+ *     (concurrent calls on different streams must not share output or workspace
+ *     buffers).  The one piece of state: moe_layer creates, on its first call on a
+ *     device, one non-blocking side stream and two events there (kept until the process
+ *     ends) and runs the shared expert on that stream, forked from and joined back into
+ *     `stream` with the events; if they cannot be created it runs everything on
+ *     `stream`.  Its enqueue sequence holds a per-device lock.
  *   - The caller owns every buffer.  Weights and inputs are read-only.
  *   - All argument checks happen on the host before any launch; a failing check
  *     returns its status and writes nothing.  MOE_ERR_LAUNCH reports a failed launch
@@ -220,6 +224,8 @@ moe_status moe_silu_mul(int32_t M, int32_t S, const void* gu, void* out, void* s
    precision chain of the [wide] module summary: router GEMM -> top-K -> lists/units ->
    latent down (BF16) -> MXFP8 latent -> grouped experts -> Finalize -> RMSNorm ->
    shared expert (gate_up, SiLU-and-mul, down) -> out = BF16(shared + normed W_up^T).
+   The shared expert runs on an internal side stream beside the routed path (see the
+   conventions above); the result does not depend on the overlap.
    x [T, H] BF16 -> out [T, H] BF16.  workspace >= moe_workspace_size(d) bytes; its layout
    (moe_workspace_layout) exposes every intermediate for inspection. */
 moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* x, void* out,

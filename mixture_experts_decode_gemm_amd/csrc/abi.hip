@@ -1,6 +1,9 @@
 // abi.hip -- the C ABI of libmoedecode (include/moedecode.h): host-side argument
-// checks, workspace layout, and the layer's launch sequence on one stream.
-// Nothing here allocates, frees or synchronises.
+// checks, workspace layout, and the layer's launch sequence.  Nothing here allocates
+// device memory, frees or synchronises; moe_layer keeps one side stream and two events
+// per device (created on its first call on that device) to run the shared expert beside
+// the routed path.
+#include <mutex>
 #include <string.h>
 
 #include "moedecode.h"
@@ -48,7 +51,7 @@ moe_status check_dims(const moe_dims* d) {
 
 struct Layout {
     size_t off[MOE_WS_FIELDS];
-    size_t gu, act, uni, total;
+    size_t gu, act, uni, uni_side, total;
 };
 
 Layout layout(const moe_dims* d) {
@@ -72,17 +75,48 @@ Layout layout(const moe_dims* d) {
     at += up256(T * S * 2);
     lo.uni = at;
     const int Tm = d->max_tokens;
+    // scratch of the routed path (router, latent down and up GEMMs, list bitmaps) and,
+    // apart from it, of the shared expert's GEMMs, which run concurrently on a side stream
     size_t u = 0;
-    const size_t g[5] = {gemm_scratch_bytes(Tm, d->experts, d->hidden),
+    const size_t g[3] = {gemm_scratch_bytes(Tm, d->experts, d->hidden),
                          gemm_scratch_bytes(Tm, d->latent, d->hidden),
-                         gemm_scratch_bytes(Tm, 2 * d->shared_inter, d->hidden),
-                         gemm_scratch_bytes(Tm, d->hidden, d->shared_inter),
                          gemm_scratch_bytes(Tm, d->hidden, d->latent)};
     for (size_t v : g) u = v > u ? v : u;
     const size_t ls = lists_scratch_bytes(Tm, d->experts);
     u = ls > u ? ls : u;
-    lo.total = at + up256(u);
+    at += up256(u);
+    lo.uni_side = at;
+    const size_t g2 = gemm_scratch_bytes(Tm, 2 * d->shared_inter, d->hidden);
+    const size_t g3 = gemm_scratch_bytes(Tm, d->hidden, d->shared_inter);
+    at += up256(g2 > g3 ? g2 : g3);
+    lo.total = at;
     return lo;
+}
+
+// One side stream and a fork/join event pair per device, created on first use and kept
+// until the process ends.  The mutex serialises the enqueue sequence of concurrent
+// moe_layer calls on one device (an event must be waited for before it is re-recorded).
+constexpr int kMaxDevices = 64;
+struct SideStream {
+    std::mutex mu;
+    bool tried = false, ok = false;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[kMaxDevices];
+
+SideStream* side_stream() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream& ss = g_side[dev];
+    std::lock_guard<std::mutex> lock(ss.mu);
+    if (!ss.tried) {
+        ss.tried = true;
+        ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+                hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+                hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+    }
+    return ss.ok ? &ss : nullptr;
 }
 
 }  // namespace
@@ -319,6 +353,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     void* gu = ws + lo.gu;
     void* act = ws + lo.act;
     void* uni = ws + lo.uni;
+    void* uni_side = ws + lo.uni_side;
 
     const int T = d->tokens, H = d->hidden, L = d->latent, E = d->experts, K = d->top_k;
     const int S = d->shared_inter, I = d->expert_inter;
@@ -327,12 +362,28 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     do {                                                \
         if ((call) != hipSuccess) return MOE_ERR_LAUNCH; \
     } while (0)
+    // The shared expert depends on x only: it runs on the side stream ([wide] module
+    // summary and [ep] module summary: the shared expert on a side stream beside the
+    // routed experts), joined before the up-projection adds into its output.  Without a
+    // side stream it runs in order on `s`.
+    SideStream* ss = side_stream();
+    std::unique_lock<std::mutex> side_lock;
+    if (ss) side_lock = std::unique_lock<std::mutex>(ss->mu);
+    hipStream_t sh = ss ? ss->s : s;
+    if (ss) {
+        MOE_TRY(hipEventRecord(ss->fork, s));
+        MOE_TRY(hipStreamWaitEvent(sh, ss->fork, 0));
+    }
+    MOE_TRY(launch_gemm(T, 2 * S, H, x, w->w_shared_gu, gu, nullptr, 1, uni_side, sh));
+    MOE_TRY(launch_silu_mul(T, S, gu, act, sh));
+    MOE_TRY(launch_gemm(T, H, S, act, w->w_shared_down, shared, nullptr, 1, uni_side, sh));
+    if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
     // routing: FP32 router GEMM, sigmoid top-K, lists and unit windows
-    MOE_TRY(launch_gemm(T, E, H, x, w->w_gate, logits, nullptr, 0, uni, s));
+    MOE_TRY(launch_gemm(T, E, H, x, w->w_gate, logits, nullptr, 0, uni, s, 0, true));
     MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts, s));
     MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, s));
     // latent down (one BF16 rounding), MXFP8 latent, grouped experts, Finalize
-    MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s));
+    MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s, 0, true));
     if (mx) {
         MOE_TRY(launch_quant_mxfp8(T, L, latent, codes, scales, s));
         MOE_TRY(launch_ffn_mx(T, K, E, L, I, d->unit_tokens, (const uint8_t*)w->experts.w13,
@@ -345,10 +396,8 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     }
     MOE_TRY(launch_finalize(T, K, L, rows, wts, nullptr, routed, s));
     MOE_TRY(launch_rmsnorm(T, L, routed, w->norm_w, d->rms_eps, normed, s));
-    // shared expert, then the up-projection added into the shared partial (one rounding)
-    MOE_TRY(launch_gemm(T, 2 * S, H, x, w->w_shared_gu, gu, nullptr, 1, uni, s));
-    MOE_TRY(launch_silu_mul(T, S, gu, act, s));
-    MOE_TRY(launch_gemm(T, H, S, act, w->w_shared_down, shared, nullptr, 1, uni, s));
+    // the up-projection added into the shared partial (one rounding)
+    if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
     MOE_TRY(launch_gemm(T, H, L, normed, w->w_up, out, shared, 2, uni, s));
 #undef MOE_TRY
     return MOE_OK;

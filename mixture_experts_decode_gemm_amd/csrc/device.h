@@ -96,6 +96,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Raise this wavefront's issue priority (s_setprio 3).  The routing kernels are short and
+// latency-bound and run while the shared expert's GEMMs occupy every CU from another
+// stream; priority lets their waves issue first on a shared SIMD.  Stream priorities are
+// not involved.
+__device__ __forceinline__ void wave_priority_high() { __builtin_amdgcn_s_setprio(3); }
+
 // ---- wave helpers ---------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -81,11 +81,12 @@ __device__ __forceinline__ void store_out(void* out, const void* add, size_t idx
 }
 
 // MODE: 0 FP32 out, 1 BF16 out, 2 BF16 out + add; 3 FP32 split partial (out = scratch)
+// One output tile (m0, n0) over K range [kb, ke) of split z.
 template <int MODE, int NS>
-__global__ __launch_bounds__(256) void k_gemm(int M, int N, int K, int kchunk,
-                                              const uint16_t* __restrict__ x,
-                                              const uint16_t* __restrict__ w, void* out,
-                                              const void* add) {
+__device__ __forceinline__ void gemm_tile(int M, int N, int K, int m0, int n0, int z, int kb,
+                                          int ke, const uint16_t* __restrict__ x,
+                                          const uint16_t* __restrict__ w, void* out,
+                                          const void* add) {
     constexpr int BM = GEMM_BM, BN = GEMM_BN;
     constexpr int LA = BM * 8 / 256, LB = BN * 8 / 256;  // 16-byte chunks per thread per step
     // stage s: [BM rows of x][BN rows of w], 128 bytes a row; row r's chunk c at c ^ ((r>>1)&7)
@@ -93,9 +94,6 @@ __global__ __launch_bounds__(256) void k_gemm(int M, int N, int K, int kchunk,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-    const int kb = blockIdx.z * kchunk;
-    const int ke = min(K, kb + kchunk);
     const int nsteps = (ke - kb) / BK;
 
     // the direct loads of a wavefront fill 64 consecutive 16-byte LDS chunks, so LDS chunk
@@ -175,7 +173,7 @@ __global__ __launch_bounds__(256) void k_gemm(int M, int N, int K, int kchunk,
                 const int row = m0 + wm * 64 + a * 16 + 4 * g + i;
                 if (row >= M) continue;
                 if (MODE == 3) {
-                    ((float*)out)[((size_t)blockIdx.z * M + row) * N + col] = acc[a][b][i];
+                    ((float*)out)[((size_t)z * M + row) * N + col] = acc[a][b][i];
                 } else {
                     store_out<MODE>(out, add, (size_t)row * N + col, acc[a][b][i]);
                 }
@@ -183,10 +181,31 @@ __global__ __launch_bounds__(256) void k_gemm(int M, int N, int K, int kchunk,
         }
 }
 
+// Work item t = (n tile fastest, then m tile, then split); a workgroup takes items
+// blockIdx.x, blockIdx.x + gridDim.x, ... (one item each when the grid covers them all; a
+// narrower persistent grid leaves room on every CU for kernels running beside it).
+template <int MODE, int NS>
+__global__ __launch_bounds__(256) void k_gemm(int M, int N, int K, int kchunk, int S, int prio,
+                                              const uint16_t* __restrict__ x,
+                                              const uint16_t* __restrict__ w, void* out,
+                                              const void* add) {
+    if (prio) wave_priority_high();
+    const int NX = (N + GEMM_BN - 1) / GEMM_BN, MY = (M + GEMM_BM - 1) / GEMM_BM;
+    const int items = NX * MY * S;
+    for (int t = blockIdx.x; t < items; t += gridDim.x) {
+        const int nt = t % NX, mt = (t / NX) % MY, z = t / (NX * MY);
+        const int kb = z * kchunk;
+        gemm_tile<MODE, NS>(M, N, K, mt * GEMM_BM, nt * GEMM_BN, z, kb, min(K, kb + kchunk), x,
+                            w, out, add);
+        if (t + gridDim.x < items) __syncthreads();  // the next item's loads reuse the LDS
+    }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256) void k_splitk_reduce(int M, int N, int S,
                                                        const float* __restrict__ part,
                                                        void* out, const void* add) {
+    wave_priority_high();
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t total = (size_t)M * N;
     if (idx >= total) return;
@@ -196,23 +215,25 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(int M, int N, int S,
 }
 
 hipError_t launch_gemm(int M, int N, int K, const void* x, const void* w, void* out,
-                       const void* add, int mode, void* scratch, hipStream_t s) {
+                       const void* add, int mode, void* scratch, hipStream_t s, int max_wg,
+                       bool prio) {
     const Split sp = choose_split(M, N, K);
     const uint16_t* xa = (const uint16_t*)x;
     const uint16_t* wa = (const uint16_t*)w;
-    const dim3 grid((N + GEMM_BN - 1) / GEMM_BN, (M + GEMM_BM - 1) / GEMM_BM, sp.S);
+    const int items = ((N + GEMM_BN - 1) / GEMM_BN) * ((M + GEMM_BM - 1) / GEMM_BM) * sp.S;
+    const dim3 grid(max_wg > 0 && max_wg < items ? max_wg : items);
     const dim3 blk(256);
     if (sp.S == 1) {
         if (mode == 0)
-            hipLaunchKernelGGL((k_gemm<0, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
+            hipLaunchKernelGGL((k_gemm<0, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, 1, prio, xa, wa, out, add);
         else if (mode == 1)
-            hipLaunchKernelGGL((k_gemm<1, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
+            hipLaunchKernelGGL((k_gemm<1, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, 1, prio, xa, wa, out, add);
         else
-            hipLaunchKernelGGL((k_gemm<2, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa, out, add);
+            hipLaunchKernelGGL((k_gemm<2, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, 1, prio, xa, wa, out, add);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_gemm<3, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, xa, wa,
-                       scratch, (const void*)nullptr);
+    hipLaunchKernelGGL((k_gemm<3, GEMM_NS>), grid, blk, 0, s, M, N, K, sp.kchunk, sp.S, prio, xa,
+                       wa, scratch, (const void*)nullptr);
     const size_t total = (size_t)M * N;
     const int blocks = (int)((total + 255) / 256);
     const float* part = (const float*)scratch;
@@ -224,5 +245,7 @@ hipError_t launch_gemm(int M, int N, int K, const void* x, const void* w, void* 
         hipLaunchKernelGGL(k_splitk_reduce<2>, dim3(blocks), blk, 0, s, M, N, sp.S, part, out, add);
     return hipGetLastError();
 }
+
+int gemm_device_cus() { return gemm_cus(); }
 
 }  // namespace moe

@@ -42,10 +42,14 @@ hipError_t launch_ffn_bf16(int T, int K, int E, int L, int I, int unit, const vo
                            const int32_t* units, const int32_t* num_units, void* rows,
                            hipStream_t s);
 
-// dense BF16 GEMM out = x W^T (mode 0 FP32 out, 1 BF16 out, 2 BF16 out with BF16 add)
+// dense BF16 GEMM out = x W^T (mode 0 FP32 out, 1 BF16 out, 2 BF16 out with BF16 add);
+// max_wg > 0 caps the grid (a persistent grid looping over the tiles); prio raises the
+// waves' issue priority (for the routed path while the shared expert runs beside it)
 size_t gemm_scratch_bytes(int M, int N, int K);
 hipError_t launch_gemm(int M, int N, int K, const void* x, const void* w, void* out,
-                       const void* add, int mode, void* scratch, hipStream_t s);
+                       const void* add, int mode, void* scratch, hipStream_t s, int max_wg = 0,
+                       bool prio = false);
+int gemm_device_cus();
 
 hipError_t launch_rmsnorm(int rows, int cols, const void* r, const void* g, float eps, void* out,
                           hipStream_t s);

@@ -26,6 +26,7 @@ size_t lists_scratch_bytes(int T, int E) {
 __global__ __launch_bounds__(256) void k_lists_mark(int T, int K, int E,
                                                     const int32_t* __restrict__ ids,
                                                     uint32_t* __restrict__ bm) {
+    wave_priority_high();
     __shared__ uint32_t words[1024];
     const int w = blockIdx.x;
     for (int e = threadIdx.x; e < E; e += 256) words[e] = 0;
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(1024) void k_lists_scan(int T, int K, int E, int un
                                                      int32_t* __restrict__ offsets,
                                                      int4* __restrict__ units,
                                                      int32_t* __restrict__ num_units) {
+    wave_priority_high();
     __shared__ int smem[17];
     const int W = (T + 31) / 32;
     const int e = threadIdx.x;
@@ -113,6 +115,7 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
                                                     const uint32_t* __restrict__ bm,
                                                     const int32_t* __restrict__ wordoff,
                                                     int32_t* __restrict__ pairs) {
+    wave_priority_high();
     const int W = (T + 31) / 32;
     const int gid = blockIdx.x * 256 + threadIdx.x;
     if (gid >= W * E) return;

@@ -11,6 +11,7 @@ namespace moe {
 __global__ __launch_bounds__(256) void k_quant_mxfp8(long nblocks, const uint4* __restrict__ x,
                                                      uint4* __restrict__ codes,
                                                      uint8_t* __restrict__ scales) {
+    wave_priority_high();
     const long b = (long)blockIdx.x * 256 + threadIdx.x;
     if (b >= nblocks) return;
     uint32_t q[16];

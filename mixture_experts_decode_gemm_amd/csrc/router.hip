@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
                                               const float* __restrict__ bias, int renorm,
                                               float scale, int32_t* __restrict__ ids,
                                               float* __restrict__ weights) {
+    wave_priority_high();
     constexpr int PER = 16;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);

@@ -86,7 +86,7 @@ Layout layout(const moe_dims* d) {
     u = ls > u ? ls : u;
     at += up256(u);
     lo.uni_side = at;
-    const size_t g2 = gemm_scratch_bytes(Tm, 2 * d->shared_inter, d->hidden);
+    const size_t g2 = gemm_parts_bytes(Tm, 2 * d->shared_inter, d->hidden);
     const size_t g3 = gemm_scratch_bytes(Tm, d->hidden, d->shared_inter);
     at += up256(g2 > g3 ? g2 : g3);
     lo.total = at;
@@ -374,8 +374,11 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(hipEventRecord(ss->fork, s));
         MOE_TRY(hipStreamWaitEvent(sh, ss->fork, 0));
     }
-    MOE_TRY(launch_gemm(T, 2 * S, H, x, w->w_shared_gu, gu, nullptr, 1, uni_side, sh));
-    MOE_TRY(launch_silu_mul(T, S, gu, act, sh));
+    // gate/up as split-K partials; the activation adds them and rounds (the gate/up BF16
+    // values) before SiLU-and-mul
+    int s_gu = 1;
+    MOE_TRY(launch_gemm_parts(T, 2 * S, H, x, w->w_shared_gu, (float*)uni_side, sh, false, &s_gu));
+    MOE_TRY(launch_silu_mul_parts(T, S, s_gu, (const float*)uni_side, act, sh));
     MOE_TRY(launch_gemm(T, H, S, act, w->w_shared_down, shared, nullptr, 1, uni_side, sh));
     if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
     // routing: FP32 router GEMM, sigmoid top-K, lists and unit windows

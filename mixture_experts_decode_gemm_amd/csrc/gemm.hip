@@ -248,4 +248,27 @@ hipError_t launch_gemm(int M, int N, int K, const void* x, const void* w, void* 
 
 int gemm_device_cus() { return gemm_cus(); }
 
+int gemm_splits(int M, int N, int K) { return choose_split(M, N, K).S; }
+
+size_t gemm_parts_bytes(int M, int N, int K) {
+    size_t best = 0;
+    for (int mt = 1; mt <= (M + GEMM_BM - 1) / GEMM_BM; ++mt) {
+        const int m = mt * GEMM_BM < M ? mt * GEMM_BM : M;
+        const size_t b = (size_t)choose_split(m, N, K).S * m * N * sizeof(float);
+        if (b > best) best = b;
+    }
+    return best;
+}
+
+hipError_t launch_gemm_parts(int M, int N, int K, const void* x, const void* w, float* parts,
+                             hipStream_t s, bool prio, int* S) {
+    const Split sp = choose_split(M, N, K);
+    const int items = ((N + GEMM_BN - 1) / GEMM_BN) * ((M + GEMM_BM - 1) / GEMM_BM) * sp.S;
+    hipLaunchKernelGGL((k_gemm<3, GEMM_NS>), dim3(items), dim3(256), 0, s, M, N, K, sp.kchunk,
+                       sp.S, prio ? 1 : 0, (const uint16_t*)x, (const uint16_t*)w, (void*)parts,
+                       (const void*)nullptr);
+    *S = sp.S;
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -50,6 +50,14 @@ hipError_t launch_gemm(int M, int N, int K, const void* x, const void* w, void* 
                        const void* add, int mode, void* scratch, hipStream_t s, int max_wg = 0,
                        bool prio = false);
 int gemm_device_cus();
+// the GEMM's FP32 split-K partials [S][M][N] only (S >= 1 returned), for a consumer that
+// adds them in split order itself; gemm_parts_bytes(M, N, K) covers every token count <= M
+int gemm_splits(int M, int N, int K);
+size_t gemm_parts_bytes(int M, int N, int K);
+hipError_t launch_gemm_parts(int M, int N, int K, const void* x, const void* w, float* parts,
+                             hipStream_t s, bool prio, int* S);
+hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, void* out,
+                                 hipStream_t s);
 
 hipError_t launch_rmsnorm(int rows, int cols, const void* r, const void* g, float eps, void* out,
                           hipStream_t s);

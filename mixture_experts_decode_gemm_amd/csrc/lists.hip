@@ -126,9 +126,16 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
         const int j = __ffs((int)word) - 1;
         word &= word - 1;
         const int t = w * 32 + j;
-        int k = 0;
-        while (ids[(size_t)t * K + k] != e) ++k;  // the bit guarantees a match
-        pairs[pos++] = t * K + k;
+        // the token's ids are loaded together (no chain of dependent loads); the first
+        // slot holding e is the one the bit stands for
+        const int32_t* row = ids + (size_t)t * K;
+        int32_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = k < K ? row[k] : -1;
+        int kk = 0;
+#pragma unroll
+        for (int k = 15; k >= 0; --k) kk = v[k] == e ? k : kk;
+        pairs[pos++] = t * K + kk;
     }
 }
 

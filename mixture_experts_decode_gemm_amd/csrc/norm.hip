@@ -71,6 +71,50 @@ __global__ __launch_bounds__(256) void k_silu_mul(int M, int S8, const uint4* __
     out[gid] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// The same from the gate/up GEMM's nsplit FP32 split-K partials [nsplit][M][2S]: each
+// gate and up value is the split-order sum rounded once to BF16 (the GEMM's output), then
+// as above.
+__global__ __launch_bounds__(256) void k_silu_mul_parts(int M, int S8, int nsplit,
+                                                        const float4* __restrict__ parts,
+                                                        uint4* __restrict__ out) {
+    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (long)M * S8) return;
+    const long m = gid / S8, c = gid - m * S8;
+    const long zs = (long)M * S8 * 4;                  // float4s per split (M x 2S floats)
+    const float4* gp = parts + m * S8 * 4 + c * 2;     // 8 gate floats of this thread
+    const float4* up = gp + S8 * 2;                    // 8 up floats
+    float gv[8], uv[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float4 a = gp[h], b = up[h];
+        for (int z = 1; z < nsplit; ++z) {
+            const float4 a2 = gp[z * zs + h], b2 = up[z * zs + h];
+            a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+            b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+        }
+        gv[4 * h] = a.x; gv[4 * h + 1] = a.y; gv[4 * h + 2] = a.z; gv[4 * h + 3] = a.w;
+        uv[4 * h] = b.x; uv[4 * h + 1] = b.y; uv[4 * h + 2] = b.z; uv[4 * h + 3] = b.w;
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t gq = pack_bf16x2(gv[2 * i], gv[2 * i + 1]);
+        const uint32_t uq = pack_bf16x2(uv[2 * i], uv[2 * i + 1]);
+        const float g0 = bf16_lo(gq), g1 = bf16_hi(gq);
+        o[i] = pack_bf16x2(g0 / (1.0f + __expf(-g0)) * bf16_lo(uq),
+                           g1 / (1.0f + __expf(-g1)) * bf16_hi(uq));
+    }
+    out[gid] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, void* out,
+                                 hipStream_t s) {
+    const long n = (long)M * (S / 8);
+    hipLaunchKernelGGL(k_silu_mul_parts, dim3((int)((n + 255) / 256)), dim3(256), 0, s, M, S / 8,
+                       nsplit, (const float4*)parts, (uint4*)out);
+    return hipGetLastError();
+}
+
 hipError_t launch_silu_mul(int M, int S, const void* gu, void* out, hipStream_t s) {
     const long n = (long)M * (S / 8);
     hipLaunchKernelGGL(k_silu_mul, dim3((int)((n + 255) / 256)), dim3(256), 0, s, M, S / 8,

@@ -5,9 +5,9 @@
 // One wavefront per token.  Each lane owns experts lane, lane+64, ... (<= 16 per lane,
 // E <= 1024) and builds 64-bit selection keys (order-preserving bits of the FP32 key
 // s + bias, then the complemented expert id so that equal keys prefer the lower id).
-// K rounds of a wave-wide maximum (xor shuffles) pick the winners in descending order;
-// the winner's lane clears its key.  Lane k keeps slot k's score; the slot-order FP32
-// sum, the divide and the routed scale follow.
+// K rounds of a wave-wide maximum (DPP, then readlane) pick the winners in descending
+// order; the winner's lane clears its key.  Lane k keeps slot k's score; the slot-order
+// FP32 sum, the divide and the routed scale follow.
 //
 // The sigmoid is 1/(1 + E(-x)) with E a defined exponential (Cody-Waite reduction with a
 // 16-significant-bit head of ln 2, degree-7 Taylor polynomial by Horner's rule, scaling
@@ -50,7 +50,32 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* __restrict__ logits,
+// Wave-wide maximum of 64-bit keys (hi, lo), returned in every lane: DPP row shifts by
+// 1, 2, 4, 8 leave each row's maximum in its lane 15, row broadcasts 15 and 31 carry them
+// to lane 63, and a readlane makes it uniform.  Lanes outside a shift's reach combine
+// with 0, the identity (every live key is nonzero).
+__device__ __forceinline__ void dpp_step(uint32_t& h, uint32_t& l, uint32_t oh, uint32_t ol) {
+    const bool gt = oh > h || (oh == h && ol > l);
+    h = gt ? oh : h;
+    l = gt ? ol : l;
+}
+#define MOE_DPP(ctrl, rmask)                                                                   \
+    dpp_step(h, l, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, ctrl, rmask, 0xf, false), \
+             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l, ctrl, rmask, 0xf, false))
+__device__ __forceinline__ void wave_max64(uint32_t& h, uint32_t& l) {
+    MOE_DPP(0x111, 0xf);  // row_shr:1
+    MOE_DPP(0x112, 0xf);  // row_shr:2
+    MOE_DPP(0x114, 0xf);  // row_shr:4
+    MOE_DPP(0x118, 0xf);  // row_shr:8
+    MOE_DPP(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    MOE_DPP(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+    h = (uint32_t)__builtin_amdgcn_readlane((int)h, 63);
+    l = (uint32_t)__builtin_amdgcn_readlane((int)l, 63);
+}
+#undef MOE_DPP
+
+// One wavefront per token.
+__global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* __restrict__ src,
                                               const float* __restrict__ bias, int renorm,
                                               float scale, int32_t* __restrict__ ids,
                                               float* __restrict__ weights) {
@@ -59,14 +84,13 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // uniform per wavefront
-    const float* lg = logits + (size_t)t * E;
     uint32_t khi[PER], klo[PER];
     float sc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = j * 64 + lane;
         if (e < E) {
-            const float s = sigmoid_defined(lg[e]);
+            const float s = sigmoid_defined(src[(size_t)t * E + e]);
             sc[j] = s;
             khi[j] = order_bits(__fadd_rn(s, bias[e]));
             klo[j] = ~(uint32_t)e;
@@ -81,38 +105,30 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
     for (int k = 0; k < K; ++k) {
         uint32_t bh = 0, bl = 0;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const bool gt = khi[j] > bh || (khi[j] == bh && klo[j] > bl);
-            bh = gt ? khi[j] : bh;
-            bl = gt ? klo[j] : bl;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const uint32_t oh = (uint32_t)__shfl_xor((int)bh, off, 64);
-            const uint32_t ol = (uint32_t)__shfl_xor((int)bl, off, 64);
-            const bool gt = oh > bh || (oh == bh && ol > bl);
-            bh = gt ? oh : bh;
-            bl = gt ? ol : bl;
-        }
-        const int win = (int)(~bl);
-        const int owner = win & 63;
-        float s_own = 0.0f;
+        for (int j = 0; j < PER; ++j) dpp_step(bh, bl, khi[j], klo[j]);
+        wave_max64(bh, bl);
+        const int win = (int)(~bl);  // uniform
+        const int owner = win & 63, jw = win >> 6;
+        float sel = 0.0f;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            if (j * 64 + lane == win) {
-                s_own = sc[j];
-                khi[j] = 0;
-                klo[j] = 0;
+            if (j == jw) {
+                sel = sc[j];
+                if (lane == owner) {
+                    khi[j] = 0;
+                    klo[j] = 0;
+                }
             }
         }
-        const float s_win = __shfl(s_own, owner, 64);
+        const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel), owner));
         if (lane == k) {
             mine = s_win;
             my_id = win;
         }
     }
     float sum = 0.0f;
-    for (int k = 0; k < K; ++k) sum = __fadd_rn(sum, __shfl(mine, k, 64));
+    for (int k = 0; k < K; ++k)
+        sum = __fadd_rn(sum, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), k)));
     if (lane < K) {
         float w = renorm ? mine / sum : mine;
         w = __fmul_rn(w, scale);

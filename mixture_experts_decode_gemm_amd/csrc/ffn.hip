@@ -240,10 +240,26 @@ constexpr int RED_FLOATS = 16 * RED_TILE;
 // 32-column block: the four partials are added in wavefront order, act = silu(gate) * up
 // in FP32, the block's amax is a max over the 16 lanes of that token (lane shuffles), and
 // the two E4M3 codes go out as one 16-bit store, the E8M0 scale from the lane holding c=0.
-__device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float* __restrict__ red,
-                                            bool store, int total, int n0, int pair, int j, int I,
-                                            uint8_t* __restrict__ hid,
-                                            uint8_t* __restrict__ hid_scales) {
+// one thread's share of a token group's MXFP8 hidden, computed but not yet stored
+struct UpOut {
+    uint32_t code2;  // two E4M3 codes (columns c, c+1)
+    uint32_t scale;  // the E8M0 byte (stored by the lane with c = 0)
+    size_t at;       // byte offset of the codes in hid (p * I + 32 j + c)
+    size_t sat;      // byte offset of the scale in hid_scales
+    bool ok, first;  // store at all; this lane holds c = 0
+};
+
+__device__ __forceinline__ void up_store(const UpOut& o, uint8_t* __restrict__ hid,
+                                         uint8_t* __restrict__ hid_scales) {
+    if (o.ok) {
+        *(uint16_t*)(hid + o.at) = (uint16_t)o.code2;
+        if (o.first) hid_scales[o.sat] = (uint8_t)o.scale;
+    }
+}
+
+__device__ __forceinline__ UpOut up_epilogue(const v4f (&acc)[4], float* __restrict__ red,
+                                             bool store, int total, int n0, int pair, int j,
+                                             int I) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -275,16 +291,19 @@ __device__ __forceinline__ void up_epilogue(const v4f (&acc)[4], float* __restri
     const int X = mx_block_exponent(mag);
     const uint32_t q0 = e4m3_rne_sat(ldexpf(a0, -X)), q1 = e4m3_rne_sat(ldexpf(a1, -X));
     const int p = __shfl(pair, n, 64);  // lane n of every wavefront holds token n's pair
-    if (store && n0 + n < total) {
-        *(uint16_t*)(hid + (size_t)p * I + j * UP_COLS + c) = (uint16_t)(q0 | (q1 << 8));
-        if (c == 0) hid_scales[(size_t)p * (I / 32) + j] = (uint8_t)(X + 127);
-    }
+    UpOut o;
+    o.code2 = q0 | (q1 << 8);
+    o.scale = (uint32_t)(X + 127);
+    o.at = (size_t)p * I + j * UP_COLS + c;
+    o.sat = (size_t)p * (I / 32) + j;
+    o.ok = store && n0 + n < total;
+    o.first = c == 0;
+    return o;
 }
 
 template <int SPW>
-__device__ __forceinline__ void up_group(UpStage<SPW>& st, int n0, int I, bool store,
-                                         uint8_t* __restrict__ hid,
-                                         uint8_t* __restrict__ hid_scales, float* red) {
+__device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, int n0, int I, bool store,
+                                          float* red) {
     const int g = (threadIdx.x & 63) >> 4;
     v4f acc[4];
 #pragma unroll
@@ -298,26 +317,34 @@ __device__ __forceinline__ void up_group(UpStage<SPW>& st, int n0, int I, bool s
             acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), st.b[i], acc[m],
                                   (int)(st.ws[m][i] >> (8 * g)), sb);
     }
-    up_epilogue(acc, red, store, st.un.w, n0, st.pair, st.j, I, hid, hid_scales);
+    return up_epilogue(acc, red, store, st.un.w, n0, st.pair, st.j, I);
 }
 
+// All token groups of one item.  The first group's result is returned unstored (the
+// caller stores it after the next item's loads: stores and loads share one counter, so a
+// store issued before them would be waited for with them); later groups of a hot expert
+// are stored at once, and then the first group's too.
 template <int SPW>
-__device__ __forceinline__ void up_compute(UpStage<SPW>& st, int K, int I, bool store,
-                                           const uint8_t* __restrict__ codes,
-                                           const uint8_t* __restrict__ scales,
-                                           const int32_t* __restrict__ pairs,
-                                           uint8_t* __restrict__ hid,
-                                           uint8_t* __restrict__ hid_scales, float* red,
-                                           int& rb) {
+__device__ __forceinline__ UpOut up_compute(UpStage<SPW>& st, int K, int I, bool store,
+                                            const uint8_t* __restrict__ codes,
+                                            const uint8_t* __restrict__ scales,
+                                            const int32_t* __restrict__ pairs,
+                                            uint8_t* __restrict__ hid,
+                                            uint8_t* __restrict__ hid_scales, float* red,
+                                            int& rb) {
     const int r16 = threadIdx.x & 15;
-    up_group(st, 0, I, store, hid, hid_scales, red + rb * RED_FLOATS);
+    UpOut first = up_group(st, 0, I, store, red + rb * RED_FLOATS);
     rb ^= 1;
+    if (st.un.w <= 16) return first;
+    up_store(first, hid, hid_scales);
+    first.ok = false;
     for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later token groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
         up_issue_acts(st, K, codes, scales);
-        up_group(st, n0, I, store, hid, hid_scales, red + rb * RED_FLOATS);
+        up_store(up_group(st, n0, I, store, red + rb * RED_FLOATS), hid, hid_scales);
         rb ^= 1;
     }
+    return first;
 }
 
 template <int SPW, bool PACKED>
@@ -347,13 +374,16 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
         // compute; otherwise the scheduler interleaves them into it)
         up_issue_weights<SPW, PACKED>(B, b_real ? item + G : item, nt, I, w13, s13, pairs, units);
         __builtin_amdgcn_sched_barrier(0);
-        up_compute(A, K, I, true, codes, scales, pairs, hid, hid_scales, red, rb);
+        const UpOut oa = up_compute(A, K, I, true, codes, scales, pairs, hid, hid_scales, red, rb);
         up_issue_acts(B, K, codes, scales);
         const int na = item + 2 * G < items ? item + 2 * G : item;
         up_issue_weights<SPW, PACKED>(A, na, nt, I, w13, s13, pairs, units);
         __builtin_amdgcn_sched_barrier(0);
-        up_compute(B, K, I, b_real, codes, scales, pairs, hid, hid_scales, red, rb);
+        up_store(oa, hid, hid_scales);  // behind the loads just issued
+        const UpOut ob = up_compute(B, K, I, b_real, codes, scales, pairs, hid, hid_scales, red, rb);
         up_issue_acts(A, K, codes, scales);
+        __builtin_amdgcn_sched_barrier(0);
+        up_store(ob, hid, hid_scales);
     }
 }
 
@@ -464,10 +494,18 @@ __device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st,
     load_dwords<IS>(hid_scales + (size_t)st.pair * SROW, st.bs);
 }
 
+// The wavefront's output block is 16 tokens x 16*MT columns of BF16.  It is staged in
+// the wavefront's own LDS area ([token][column], rows padded by 16 bytes) and written
+// back so that each store instruction covers whole 128-byte lines: lane l takes token
+// 4q + l/16 and the 16 bytes at column 8 (l mod 16) .. of the block (MT = 8: 256 bytes a
+// token, two full lines).  No other wavefront touches the area, so no barrier is needed.
+template <int MT>
+constexpr int down_stage_row() { return 32 * MT + 16; }
+
 template <int IS, int MT>
-__device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L, bool store,
-                                           uint16_t* __restrict__ rows) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void down_mfma_stage(DownStage<IS, MT>& st, uint8_t* stage) {
+    constexpr int ROWB = down_stage_row<MT>();
+    const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g = lane >> 4;
     v4f acc[MT];
 #pragma unroll
@@ -478,30 +516,55 @@ __device__ __forceinline__ void down_group(DownStage<IS, MT>& st, int n0, int L,
         for (int m = 0; m < MT; ++m)
             acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][s]), st.b[s], acc[m],
                                   (int)(st.sw[m][s] >> (8 * g)), (int)(st.bs[s] >> (8 * g)));
-    if (store && n0 + r16 < st.un.w) {
+    // acc[m][i] = out[token r16][column m*16 + 4g + i]
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int row = st.j * (64 * MT) + wave * (16 * MT) + m * 16 + 4 * g;
-            uint2 o;
-            o.x = pack_bf16x2(acc[m][0], acc[m][1]);
-            o.y = pack_bf16x2(acc[m][2], acc[m][3]);
-            *(uint2*)(rows + (size_t)st.pair * L + row) = o;
-        }
+    for (int m = 0; m < MT; ++m) {
+        uint2 o;
+        o.x = pack_bf16x2(acc[m][0], acc[m][1]);
+        o.y = pack_bf16x2(acc[m][2], acc[m][3]);
+        *(uint2*)(stage + r16 * ROWB + (m * 16 + 4 * g) * 2) = o;
     }
 }
 
+// write the staged block of token group n0 (pair ids in st.pair) to the rows
+template <int IS, int MT>
+__device__ __forceinline__ void down_store(const DownStage<IS, MT>& st, int n0, int L, bool store,
+                                           uint16_t* __restrict__ rows, const uint8_t* stage) {
+    constexpr int ROWB = down_stage_row<MT>();
+    constexpr int LANES_PER_TOKEN = 2 * MT;  // 16-byte pieces per token
+    constexpr int TOKENS_PER_STORE = 64 / LANES_PER_TOKEN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col0 = st.j * (64 * MT) + wave * (16 * MT);
+#pragma unroll
+    for (int q = 0; q < 16 / TOKENS_PER_STORE; ++q) {
+        const int tk = q * TOKENS_PER_STORE + lane / LANES_PER_TOKEN;
+        const int piece = lane % LANES_PER_TOKEN;
+        const uint4 v = *(const uint4*)(stage + tk * ROWB + piece * 16);
+        const int p = __shfl(st.pair, tk, 64);  // lane tk holds token tk's pair
+        if (store && n0 + tk < st.un.w)
+            *(uint4*)(rows + (size_t)p * L + col0 + piece * 8) = v;
+    }
+}
+
+// The item's first token group is computed and left staged (its store is issued by the
+// caller after the next item's loads, so that waiting for those loads never waits for
+// these stores: stores count in the same counter); later groups of a hot expert are
+// stored at once.
 template <int IS, int MT>
 __device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L, bool store,
                                              const uint8_t* __restrict__ hid,
                                              const uint8_t* __restrict__ hid_scales,
                                              const int32_t* __restrict__ pairs,
-                                             uint16_t* __restrict__ rows) {
+                                             uint16_t* __restrict__ rows, uint8_t* stage) {
     const int r16 = threadIdx.x & 15;
-    down_group(st, 0, L, store, rows);
+    down_mfma_stage(st, stage);
+    if (st.un.w <= 16) return;
+    down_store(st, 0, L, store, rows, stage);
     for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later pair groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
         down_issue_acts(st, hid, hid_scales);
-        down_group(st, n0, L, store, rows);
+        down_mfma_stage(st, stage);
+        down_store(st, n0, L, store, rows, stage);
     }
 }
 
@@ -511,6 +574,8 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     const uint8_t* __restrict__ hid, const uint8_t* __restrict__ hid_scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
     const int32_t* __restrict__ num_units, uint16_t* __restrict__ rows) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][16 * (32 * MT + 16)];
+    uint8_t* stage = stage_all[threadIdx.x >> 6];
     const int nt = L / (64 * MT);
     const int items = num_units[2] * nt;
     const int G = gridDim.x;
@@ -526,13 +591,21 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         down_issue_weights<IS, MT, PACKED>(B, b_real ? item + G : item, nt, L, w2, s2, pairs,
                                            units);
         __builtin_amdgcn_sched_barrier(0);
-        down_compute(A, L, true, hid, hid_scales, pairs, rows);
+        down_compute(A, L, true, hid, hid_scales, pairs, rows, stage);
         down_issue_acts(B, hid, hid_scales);
+        const bool a_staged = A.un.w <= 16;
+        const int a_j = A.j, a_pair = A.pair, a_w = A.un.w;
         const int na = item + 2 * G < items ? item + 2 * G : item;
         down_issue_weights<IS, MT, PACKED>(A, na, nt, L, w2, s2, pairs, units);
         __builtin_amdgcn_sched_barrier(0);
-        down_compute(B, L, b_real, hid, hid_scales, pairs, rows);
+        if (a_staged) {  // item A's deferred store, behind the loads just issued
+            DownStage<IS, MT> done;
+            done.j = a_j; done.pair = a_pair; done.un.w = a_w;
+            down_store(done, 0, L, true, rows, stage);
+        }
+        down_compute(B, L, b_real, hid, hid_scales, pairs, rows, stage);
         down_issue_acts(A, hid, hid_scales);
+        if (B.un.w <= 16) down_store(B, 0, L, b_real, rows, stage);
     }
 }
 

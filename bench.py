@@ -76,7 +76,7 @@ def parse():
                         "the reference for scaling the HBM byte counters")
     p.add_argument("--sweep", action="store_true", help="also time T in {65,130,255,510,1020}")
     p.add_argument("--row-major", action="store_true",
-                   help="run the experts on the row-major weights instead of the packed layout")
+                   help="run on the row-major expert and dense weights instead of the packed layouts")
     return p.parse_args()
 
 
@@ -112,12 +112,15 @@ def main():
         pk = moe.moe_pack_expert_weights(moe.dims(1, 1), dw["w13"], dw["s13"], dw["w2"], dw["s2"])
         dw.update(w13=pk[0], s13=pk[1], w2=pk[2], s2=pk[3])
         fmt = moe.MOE_FMT_MXFP4_MXFP8_PACKED
+        for k in ("w_gate", "w_down", "w_shared_gu", "w_shared_dn", "w_up"):  # dense weights too
+            dw[k] = moe.moe_pack_dense_weight(dw[k])
         torch.cuda.synchronize()
     print(f"# inputs generated and resident in HBM in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
     lw = moe.layer_weights(dw["w_gate"], dw["bias"], dw["w_down"], dw["w_shared_gu"],
                            dw["w_shared_dn"], dw["norm_w"], dw["w_up"], dw["w13"], dw["s13"],
-                           dw["w2"], dw["s2"])
+                           dw["w2"], dw["s2"],
+                           dense_format=moe.MOE_DENSE_ROWMAJOR if a.row_major else moe.MOE_DENSE_PACKED)
     dmax = moe.dims(1020, 1020, expert_format=fmt)
     ws = torch.zeros(moe.moe_workspace_size(dmax), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -201,7 +204,7 @@ def main():
         "config": {"workload": f"wide latent-MoE decode layer, T={T} tokens, hidden 7168, latent "
                                f"3584, 896 MXFP4 experts top-16, expert inter 512, shared inter "
                                f"6144, {'Zipf' if a.zipf else 'uniform'} routing bias, "
-                               f"{'row-major' if a.row_major else 'packed'} expert weights",
+                               f"{'row-major' if a.row_major else 'packed'} expert and dense weights",
                    "tokens": T, "touched_experts": D, "units": nu},
         "layer_roofline": {"bound": "hbm", "weight_bytes": layer_bytes,
                            "achieved": layer_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -89,9 +89,16 @@ typedef struct {
     const void *w13, *s13, *w2, *s2;
 } moe_expert_weights;
 
+/* dense weight format of moe_layer_weights */
+enum { MOE_DENSE_ROWMAJOR = 0, /* BF16 [N, K] row-major, as the pages state the weights */
+       MOE_DENSE_PACKED = 1 }; /* the same values reordered by moe_pack_dense_weight */
+
 /* Layer weights (device): w_gate BF16 [E, H]; bias FP32 [E] (the e_score correction
    bias); w_down BF16 [L, H]; w_shared_gu BF16 [2S, H] (gate rows first);
-   w_shared_down BF16 [H, S]; norm_w BF16 [L]; w_up BF16 [H, L]. */
+   w_shared_down BF16 [H, S]; norm_w BF16 [L]; w_up BF16 [H, L].  dense_format tells the
+   layout of the five BF16 matrices: all row-major, or all packed (each matrix packed on
+   its own by moe_pack_dense_weight; needs E, L, 2S and H multiples of 64 and H, S, L
+   multiples of 128).  The results are identical in both layouts. */
 typedef struct {
     const void* w_gate;
     const float* bias;
@@ -101,6 +108,7 @@ typedef struct {
     const void* norm_w;
     const void* w_up;
     moe_expert_weights experts;
+    int32_t dense_format;
 } moe_layer_weights;
 
 /* Router GEMM and sigmoid top-K ([ep] EpMoeLayer.topk and stock_order; [wide] WideRoute).
@@ -214,6 +222,16 @@ moe_status moe_linear(int32_t M, int32_t N, int32_t K, const void* x, const void
                       const void* add, int32_t mode, void* workspace, size_t ws_bytes,
                       void* stream);
 size_t moe_linear_workspace_size(int32_t M, int32_t N, int32_t K);
+
+/* Load-time reordering of one dense BF16 weight W [N, K] into the packed layout
+   (MOE_DENSE_PACKED; [wide] WideMoE prepares its front weights once, ahead of the steps,
+   and [ep] packs the front the same way).  The output holds the same N*K values as 1 KiB
+   blocks [N/64 row groups][K/64 K stages][tile 2][K step 4][lane 64][8 BF16]: lane l of
+   block (g, s, i, q) holds row 64g + 32i + l%32, columns 64s + 16q + 8(l/32) .. +8 -- the
+   A operand of one 32x32x16 BF16 MFMA, so that every weight load of the dense kernels is
+   a contiguous 1 KiB block per wavefront.  N % 64 == 0, K % 128 == 0; out (N*K BF16,
+   caller-owned) must not overlap w.  Enqueued on `stream`. */
+moe_status moe_pack_dense_weight(int32_t N, int32_t K, const void* w, void* out, void* stream);
 
 /* Shared-expert gated activation ([ep] EpMoeLayer.gate_up; SiLU-and-mul stands in for
    the pages' undefined SiTU): out[m,j] = BF16(silu(gu[m,j]) * gu[m,S+j]), FP32 math;

@@ -21,6 +21,7 @@ STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_ALIGN", "MOE
 MOE_FMT_MXFP4_MXFP8, MOE_FMT_BF16, MOE_FMT_MXFP4_MXFP8_PACKED = 0, 1, 2
 MOE_LOGITS_GIVEN = 1
 MOE_LINEAR_F32, MOE_LINEAR_BF16, MOE_LINEAR_ADD_BF16 = 0, 1, 2
+MOE_DENSE_ROWMAJOR, MOE_DENSE_PACKED = 0, 1
 WORKSPACE_FIELDS = ["logits", "ids", "weights", "counts", "offsets", "pairs", "units", "num_units",
                     "latent", "codes", "scales", "rows", "routed", "shared", "normed", "hidden",
                     "hidden_scales", "scratch"]
@@ -47,13 +48,15 @@ class moe_expert_weights(C.Structure):
 class moe_layer_weights(C.Structure):
     _fields_ = [("w_gate", C.c_void_p), ("bias", C.c_void_p), ("w_down", C.c_void_p),
                 ("w_shared_gu", C.c_void_p), ("w_shared_down", C.c_void_p),
-                ("norm_w", C.c_void_p), ("w_up", C.c_void_p), ("experts", moe_expert_weights)]
+                ("norm_w", C.c_void_p), ("w_up", C.c_void_p), ("experts", moe_expert_weights),
+                ("dense_format", C.c_int32)]
 
 
 EXPORTS = ["moe_router_topk", "moe_router_workspace_size", "moe_build_lists",
            "moe_lists_workspace_size", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_stages", "moe_pack_expert_weights",
            "moe_ffn_workspace_size", "moe_finalize", "moe_rmsnorm", "moe_linear",
-           "moe_linear_workspace_size", "moe_silu_mul", "moe_layer", "moe_workspace_size",
+           "moe_linear_workspace_size", "moe_pack_dense_weight", "moe_silu_mul", "moe_layer",
+           "moe_workspace_size",
            "moe_workspace_layout", "moe_version"]
 
 _lib = None
@@ -85,6 +88,7 @@ def lib():
             "moe_rmsnorm": (i32, [i32, i32, v, v, f, v, v]),
             "moe_linear": (i32, [i32, i32, i32, v, v, v, v, i32, v, sz, v]),
             "moe_linear_workspace_size": (sz, [i32, i32, i32]),
+            "moe_pack_dense_weight": (i32, [i32, i32, v, v, v]),
             "moe_silu_mul": (i32, [i32, i32, v, v, v]),
             "moe_layer": (i32, [D, C.POINTER(moe_layer_weights), v, v, v, sz, v]),
             "moe_workspace_size": (sz, [D]),
@@ -265,6 +269,16 @@ def moe_linear(x, w, out, add=None, mode=MOE_LINEAR_BF16, workspace=None, stream
     _check("moe_linear", st)
 
 
+def moe_pack_dense_weight(w, stream=None):
+    """The packed copy of a dense BF16 weight W [N, K] (MOE_DENSE_PACKED; same shape)."""
+    N, K = w.shape
+    out = torch.empty_like(w)
+    st = lib().moe_pack_dense_weight(N, K, _ptr(w, BF16, "w"), _ptr(out, BF16, "out"),
+                                     _stream(stream))
+    _check("moe_pack_dense_weight", st)
+    return out
+
+
 def moe_silu_mul(gu, out, stream=None):
     M, S2 = gu.shape
     st = lib().moe_silu_mul(M, S2 // 2, _ptr(gu, BF16, "gu"), _ptr(out, BF16, "out"),
@@ -273,12 +287,12 @@ def moe_silu_mul(gu, out, stream=None):
 
 
 def layer_weights(w_gate, bias, w_down, w_shared_gu, w_shared_down, norm_w, w_up, w13, s13, w2,
-                  s2):
+                  s2, dense_format=MOE_DENSE_ROWMAJOR):
     return moe_layer_weights(_ptr(w_gate, BF16, "w_gate"), _ptr(bias, F32, "bias"),
                              _ptr(w_down, BF16, "w_down"), _ptr(w_shared_gu, BF16, "w_shared_gu"),
                              _ptr(w_shared_down, BF16, "w_shared_down"),
                              _ptr(norm_w, BF16, "norm_w"), _ptr(w_up, BF16, "w_up"),
-                             expert_weights(w13, s13, w2, s2))
+                             expert_weights(w13, s13, w2, s2), int(dense_format))
 
 
 def moe_layer(d, weights: moe_layer_weights, x, out, workspace, stream=None):

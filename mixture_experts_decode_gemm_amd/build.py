@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.hip", "finalize.hip", "quant.hip", "router.hip", "lists.hip", "ffn.hip",
-           "gemm.hip", "norm.hip"]
+           "gemm.hip", "wgemm.hip", "norm.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", CSRC, "-I", INCLUDE]

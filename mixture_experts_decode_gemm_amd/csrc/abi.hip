@@ -77,18 +77,21 @@ Layout layout(const moe_dims* d) {
     const int Tm = d->max_tokens;
     // scratch of the routed path (router, latent down and up GEMMs, list bitmaps) and,
     // apart from it, of the shared expert's GEMMs, which run concurrently on a side stream
+    // (the sizes of both dense paths: the weight-streaming GEMM where the shapes allow it,
+    // the tiled GEMM otherwise)
+    const int Hi = d->hidden, Li = d->latent, Ei = d->experts, S2 = 2 * d->shared_inter;
     size_t u = 0;
-    const size_t g[3] = {gemm_scratch_bytes(Tm, d->experts, d->hidden),
-                         gemm_scratch_bytes(Tm, d->latent, d->hidden),
-                         gemm_scratch_bytes(Tm, d->hidden, d->latent)};
+    const size_t g[6] = {gemm_scratch_bytes(Tm, Ei, Hi),      gemm_scratch_bytes(Tm, Li, Hi),
+                         gemm_scratch_bytes(Tm, Hi, Li),      wgemm_parts_bytes(Tm, Ei + Li, Hi),
+                         wgemm_parts_bytes(Tm, Hi, Li),       lists_scratch_bytes(Tm, Ei)};
     for (size_t v : g) u = v > u ? v : u;
-    const size_t ls = lists_scratch_bytes(Tm, d->experts);
-    u = ls > u ? ls : u;
     at += up256(u);
     lo.uni_side = at;
-    const size_t g2 = gemm_parts_bytes(Tm, 2 * d->shared_inter, d->hidden);
-    const size_t g3 = gemm_scratch_bytes(Tm, d->hidden, d->shared_inter);
-    at += up256(g2 > g3 ? g2 : g3);
+    size_t us = 0;
+    const size_t g2[4] = {gemm_parts_bytes(Tm, S2, Hi), gemm_scratch_bytes(Tm, Hi, d->shared_inter),
+                          wgemm_parts_bytes(Tm, S2, Hi), wgemm_parts_bytes(Tm, Hi, d->shared_inter)};
+    for (size_t v : g2) us = v > us ? v : us;
+    at += up256(us);
     lo.total = at;
     return lo;
 }
@@ -125,9 +128,17 @@ extern "C" {
 
 const char* moe_version(void) { return "libmoedecode 0.1 (gfx950)"; }
 
+// the router GEMM: the weight-streaming kernel when the shape allows it
+bool router_fast(const moe_dims* d) { return wgemm_fits(d->experts, d->experts, d->hidden, false); }
+
+size_t router_scratch(const moe_dims* d, int M) {
+    return router_fast(d) ? wgemm_parts_bytes(M, d->experts, d->hidden)
+                          : gemm_scratch_bytes(M, d->experts, d->hidden);
+}
+
 size_t moe_router_workspace_size(const moe_dims* d) {
     if (check_dims(d) != MOE_OK) return 0;
-    return gemm_scratch_bytes(d->max_tokens, d->experts, d->hidden);
+    return router_scratch(d, d->max_tokens);
 }
 
 moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
@@ -141,11 +152,18 @@ moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
     if (!given && (!x || !w_gate)) return MOE_ERR_NULL;
     if (!al16(bias) || !al16(logits) || !al16(ids) || !al16(weights)) return MOE_ERR_ALIGN;
     if (!given && (!al16(x) || !al16(w_gate))) return MOE_ERR_ALIGN;
-    const size_t need = given ? 0 : gemm_scratch_bytes(d->tokens, d->experts, d->hidden);
+    const size_t need = given ? 0 : router_scratch(d, d->tokens);
     if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
     if (workspace && !al16(workspace)) return MOE_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (!given) {
+    if (!given && router_fast(d)) {
+        int S = 1;
+        if (launch_wgemm(d->tokens, d->experts, d->experts, d->hidden, x, w_gate, nullptr, false,
+                         (float*)workspace, s, false, &S) != hipSuccess ||
+            launch_wg_reduce(d->tokens, d->experts, d->experts, S, (const float*)workspace, logits,
+                             0, nullptr, nullptr, s, false) != hipSuccess)
+            return MOE_ERR_LAUNCH;
+    } else if (!given) {
         hipError_t e = launch_gemm(d->tokens, d->experts, d->hidden, x, w_gate, logits, nullptr, 0,
                                    workspace, s);
         if (e != hipSuccess) return MOE_ERR_LAUNCH;
@@ -276,7 +294,7 @@ moe_status moe_rmsnorm(int32_t rows, int32_t cols, const void* r, const void* g,
 
 size_t moe_linear_workspace_size(int32_t M, int32_t N, int32_t K) {
     if (M < 1 || N < 1 || K < 64 || K % 64) return 0;
-    return gemm_scratch_bytes(M, N, K);
+    return wgemm_fits(N, N, K, false) ? wgemm_parts_bytes(M, N, K) : gemm_scratch_bytes(M, N, K);
 }
 
 moe_status moe_linear(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* out,
@@ -286,10 +304,29 @@ moe_status moe_linear(int32_t M, int32_t N, int32_t K, const void* x, const void
     if (mode < MOE_LINEAR_F32 || mode > MOE_LINEAR_ADD_BF16) return MOE_ERR_FORMAT;
     if (!x || !w || !out || (mode == MOE_LINEAR_ADD_BF16 && !add)) return MOE_ERR_NULL;
     if (!al16(x) || !al16(w) || !al16(out) || (add && !al16(add))) return MOE_ERR_ALIGN;
-    const size_t need = gemm_scratch_bytes(M, N, K);
+    const bool fast = wgemm_fits(N, N, K, false);
+    const size_t need = fast ? wgemm_parts_bytes(M, N, K) : gemm_scratch_bytes(M, N, K);
     if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
     if (workspace && !al16(workspace)) return MOE_ERR_ALIGN;
-    return launch_status(launch_gemm(M, N, K, x, w, out, add, mode, workspace, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    if (fast) {
+        int S = 1;
+        if (launch_wgemm(M, N, N, K, x, w, nullptr, false, (float*)workspace, s, false, &S) !=
+            hipSuccess)
+            return MOE_ERR_LAUNCH;
+        return launch_status(launch_wg_reduce(M, N, 0, S, (const float*)workspace, nullptr, mode,
+                                              out, add, s, false));
+    }
+    return launch_status(launch_gemm(M, N, K, x, w, out, add, mode, workspace, s));
+}
+
+moe_status moe_pack_dense_weight(int32_t N, int32_t K, const void* w, void* out, void* stream) {
+    if (N < 64 || N % 64 || K < 128 || K % 128 || (long)N * K > (1L << 34)) return MOE_ERR_SHAPE;
+    if (!w || !out) return MOE_ERR_NULL;
+    if (!al16(w) || !al16(out)) return MOE_ERR_ALIGN;
+    const uintptr_t a = (uintptr_t)w, b = (uintptr_t)out, n = (uintptr_t)N * K * 2;
+    if (a < b + n && b < a + n) return MOE_ERR_SHAPE;  // overlapping buffers
+    return launch_status(launch_pack_dense(N, K, w, out, (hipStream_t)stream));
 }
 
 moe_status moe_silu_mul(int32_t M, int32_t S, const void* gu, void* out, void* stream) {
@@ -329,6 +366,17 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     for (const void* p : ptrs)
         if (!al16(p)) return MOE_ERR_ALIGN;
     if (mx && (!al16(w->experts.s13) || !al16(w->experts.s2))) return MOE_ERR_ALIGN;
+    if (w->dense_format != MOE_DENSE_ROWMAJOR && w->dense_format != MOE_DENSE_PACKED)
+        return MOE_ERR_FORMAT;
+    const bool dpack = w->dense_format == MOE_DENSE_PACKED;
+    // the weight-streaming GEMMs for every dense projection, else (row-major weights of
+    // shapes they do not take) the tiled GEMM
+    const int S2 = 2 * d->shared_inter;
+    const bool fast = wgemm_fits(d->experts + d->latent, d->experts, d->hidden, dpack) &&
+                      wgemm_fits(S2, S2, d->hidden, dpack) &&
+                      wgemm_fits(d->hidden, d->hidden, d->shared_inter, dpack) &&
+                      wgemm_fits(d->hidden, d->hidden, d->latent, dpack);
+    if (dpack && !fast) return MOE_ERR_SHAPE;
     const Layout lo = layout(d);
     if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE;
 
@@ -376,17 +424,34 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     }
     // gate/up as split-K partials; the activation adds them and rounds (the gate/up BF16
     // values) before SiLU-and-mul
-    int s_gu = 1;
-    MOE_TRY(launch_gemm_parts(T, 2 * S, H, x, w->w_shared_gu, (float*)uni_side, sh, false, &s_gu));
-    MOE_TRY(launch_silu_mul_parts(T, S, s_gu, (const float*)uni_side, act, sh));
-    MOE_TRY(launch_gemm(T, H, S, act, w->w_shared_down, shared, nullptr, 1, uni_side, sh));
+    int s_gu = 1, s_sd = 1, s_fr = 1, s_up = 1;
+    float* parts_side = (float*)uni_side;
+    float* parts = (float*)uni;
+    if (fast) {
+        MOE_TRY(launch_wgemm(T, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, dpack, parts_side, sh,
+                             false, &s_gu));
+        MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, act, sh));
+        MOE_TRY(launch_wgemm(T, H, H, S, act, w->w_shared_down, nullptr, dpack, parts_side, sh,
+                             false, &s_sd));
+        MOE_TRY(launch_wg_reduce(T, H, 0, s_sd, parts_side, nullptr, 1, shared, nullptr, sh, false));
+    } else {
+        MOE_TRY(launch_gemm_parts(T, 2 * S, H, x, w->w_shared_gu, parts_side, sh, false, &s_gu));
+        MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, act, sh));
+        MOE_TRY(launch_gemm(T, H, S, act, w->w_shared_down, shared, nullptr, 1, uni_side, sh));
+    }
     if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
-    // routing: FP32 router GEMM, sigmoid top-K, lists and unit windows
-    MOE_TRY(launch_gemm(T, E, H, x, w->w_gate, logits, nullptr, 0, uni, s, 0, true));
+    // routing: FP32 router GEMM (with the latent down in one GEMM over x: FP32 logits and
+    // the latent rounded once to BF16), sigmoid top-K, lists and unit windows
+    if (fast) {
+        MOE_TRY(launch_wgemm(T, E + L, E, H, x, w->w_gate, w->w_down, dpack, parts, s, true, &s_fr));
+        MOE_TRY(launch_wg_reduce(T, E + L, E, s_fr, parts, logits, 1, latent, nullptr, s, true));
+    } else {
+        MOE_TRY(launch_gemm(T, E, H, x, w->w_gate, logits, nullptr, 0, uni, s, 0, true));
+        MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s, 0, true));
+    }
     MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts, s));
     MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, s));
-    // latent down (one BF16 rounding), MXFP8 latent, grouped experts, Finalize
-    MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s, 0, true));
+    // MXFP8 latent, grouped experts, Finalize
     if (mx) {
         MOE_TRY(launch_quant_mxfp8(T, L, latent, codes, scales, s));
         MOE_TRY(launch_ffn_mx(T, K, E, L, I, d->unit_tokens, (const uint8_t*)w->experts.w13,
@@ -401,7 +466,12 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     MOE_TRY(launch_rmsnorm(T, L, routed, w->norm_w, d->rms_eps, normed, s));
     // the up-projection added into the shared partial (one rounding)
     if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
-    MOE_TRY(launch_gemm(T, H, L, normed, w->w_up, out, shared, 2, uni, s));
+    if (fast) {
+        MOE_TRY(launch_wgemm(T, H, H, L, normed, w->w_up, nullptr, dpack, parts, s, false, &s_up));
+        MOE_TRY(launch_wg_reduce(T, H, 0, s_up, parts, nullptr, 2, out, shared, s, false));
+    } else {
+        MOE_TRY(launch_gemm(T, H, L, normed, w->w_up, out, shared, 2, uni, s));
+    }
 #undef MOE_TRY
     return MOE_OK;
 }

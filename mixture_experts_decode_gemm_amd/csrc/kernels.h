@@ -59,6 +59,23 @@ hipError_t launch_gemm_parts(int M, int N, int K, const void* x, const void* w, 
 hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, void* out,
                                  hipStream_t s);
 
+// weight-streaming dense GEMM (wgemm.hip): FP32 split partials [S][M][N] of x W^T where
+// rows [0, N0) of W come from w0 and rows [N0, N) from w1 (row-major, or packed by
+// launch_pack_dense); *S receives the split count.  wgemm_fits tells whether the shape is
+// supported (K % 128 == 0, N0 and N - N0 multiples of 32, of 64 when packed).
+bool wgemm_fits(int N, int N0, int K, bool packed);
+int wgemm_splits(int M, int N, int K);
+size_t wgemm_parts_bytes(int M, int N, int K);
+hipError_t launch_wgemm(int M, int N, int N0, int K, const void* x, const void* w0,
+                        const void* w1, bool packed, float* parts, hipStream_t s, bool prio,
+                        int* S);
+// adds the S partials in split order: columns [0, N0) to out0 (FP32), the rest to out1 with
+// mode1 0 FP32, 1 BF16, 2 BF16 of add1 + sum
+hipError_t launch_wg_reduce(int M, int N, int N0, int S, const float* parts, float* out0,
+                            int mode1, void* out1, const void* add1, hipStream_t s, bool prio);
+// W [N, K] BF16 -> the packed layout (N % 64 == 0, K % 64 == 0)
+hipError_t launch_pack_dense(int N, int K, const void* w, void* out, hipStream_t s);
+
 hipError_t launch_rmsnorm(int rows, int cols, const void* r, const void* g, float eps, void* out,
                           hipStream_t s);
 hipError_t launch_silu_mul(int M, int S, const void* gu, void* out, hipStream_t s);

@@ -1,0 +1,355 @@
+// wgemm.hip -- the dense BF16 projections of a decode step, out = x W^T with FP32
+// accumulation (wide page, module summary and precision paragraph: BF16 dense
+// projections, FP32 router logits, the latent rounded to BF16 once; ep/layer page,
+// stock_order: the shared expert's gate_up and down, the up-projection added into the
+// shared partial with one rounding).  The router rows and the latent down rows form one
+// GEMM over x, as the wide page's front does (one FP32-out GEMM over the router rows and
+// the latent down rows, packed ahead of the step).
+//
+// Decode batches are short (M = 65 .. 1020 tokens) and the weights long (N x K up to
+// 12288 x 7168), so at M ~ 256 a projection is near the MFMA/HBM balance point: both
+// the weight stream and the matrix cores must run close to their limits.  Design:
+//  * one workgroup per CU (8 wavefronts); its tile is 256 weight rows x up to 256 tokens
+//    over a K range (split-K), the largest FP32 accumulator tile the register file holds
+//    (each wavefront: 32 rows x 256 tokens = 128 accumulators per lane);
+//  * weights go straight from HBM into VGPRs as the A operands of
+//    v_mfma_f32_32x32x16_bf16 (each wavefront streams its own 32 rows, so nothing is
+//    shared and nothing goes through LDS); packed weights make each of these loads one
+//    contiguous 1 KiB block per wavefront;
+//  * activations go global -> LDS by direct loads (two 64-deep K stages, rows
+//    XOR-swizzled in 16-byte chunks) and are read by all eight wavefronts as B operands;
+//  * the LDS reads of the next group of token tiles are issued ahead of the current
+//    group's MFMAs (scheduling groups pin that order), the next K stage's weights and
+//    activations are in flight during the current stage's MFMAs;
+//  * split-K partials go to an FP32 buffer [S][M][N]; a reduce kernel adds them in split
+//    order and applies the epilogue (FP32 out, BF16 out, BF16 out of an added BF16
+//    tensor plus the sum), or the consumer adds them itself (SiLU-and-mul).  The split
+//    count balances filling the CUs against the partial traffic it costs.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// blocks b, b + 8, b + 16, ... run on one XCD (round-robin placement); give each XCD a
+// contiguous run of work items so the workgroups sharing an activation K range share
+// that XCD's L2
+__device__ __forceinline__ int wg_xcd_item(int b, int G) {
+    const int x = b & 7, j = b >> 3, q = G >> 3, r = G & 7;
+    return x * q + (x < r ? x : r) + j;
+}
+
+struct WgArgs {
+    const uint16_t* x;   // [M, K] BF16
+    const uint16_t* w0;  // rows [0, N0): row-major [N0, K] or packed
+    const uint16_t* w1;  // rows [N0, N): row-major [N - N0, K] or packed (may be null if N0 == N)
+    float* part;         // [S][M][N] FP32
+    int M, K, N, N0, S, NX, MCH, prio;
+};
+
+// MT32: 32-token tiles computed per token chunk (1..8); PACKED: weights in the packed
+// layout of launch_pack_dense.
+template <int MT32, bool PACKED>
+__global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
+    constexpr int ROWS = (MT32 + 1) / 2 * 64;  // token rows staged (whole direct-load rounds)
+    constexpr int LA = ROWS / 64;              // direct loads per thread per K stage
+    constexpr int SLOT = ROWS * 128;           // bytes of one LDS stage (64 K x ROWS)
+    constexpr int LOOK = MT32 % 4 == 0 ? 4 : (MT32 % 3 == 0 ? 3 : (MT32 % 2 == 0 ? 2 : MT32));
+    constexpr int NG = MT32 / LOOK;  // LDS read groups per 16-deep K step
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
+    if (a.prio) wave_priority_high();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int item = wg_xcd_item(blockIdx.x, a.NX * a.S * a.MCH);
+    const int nt = item % a.NX, rest = item / a.NX;
+    const int z = rest % a.S, mc = rest / a.S;
+    const int Q = a.K / 128;  // K in pairs of stages
+    const int q0 = z * Q / a.S, q1 = (z + 1) * Q / a.S;
+    const int kb = q0 * 128, nst = (q1 - q0) * 2;
+    const int n0 = nt * 256 + wave * 32;  // this wavefront's 32 output rows
+    const int m0 = mc * 256;
+
+    // weight rows of this wavefront (past N: a valid tile, loaded but never stored)
+    const int nrow = min(n0, a.N - 32);
+    const bool second = nrow >= a.N0;
+    const uint16_t* wm = second ? a.w1 : a.w0;
+    const int wr = second ? nrow - a.N0 : nrow;
+    const uint16_t* wsrc =
+        PACKED ? wm + (size_t)(wr / 64) * (a.K / 64) * 4096 + ((wr % 64) / 32) * 2048 + lane * 8
+               : wm + (size_t)(wr + r32) * a.K + 8 * h;
+    // activation chunks: LDS chunk p = i * 512 + tid holds row p / 8, chunk (p % 8) ^ sw(row)
+    const uint16_t* asrc[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int p = i * 512 + tid, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+        asrc[i] = a.x + (size_t)min(m0 + r, a.M - 1) * a.K + 8 * c;
+    }
+    // stages past the end repeat the last one (never used), so every thread always has
+    // the same loads in flight
+    uint4 wf[2][4];
+    auto issue_w = [&](int slot, int st) {
+        const int k0 = kb + min(st, nst - 1) * 64;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            wf[slot][q] = *(const uint4*)(PACKED ? wsrc + (size_t)(k0 / 64) * 4096 + q * 512
+                                                 : wsrc + k0 + 16 * q);
+    };
+    auto issue_a = [&](int slot, int st) {
+        const int k0 = kb + min(st, nst - 1) * 64;
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + k0),
+                                             (lds_ptr)(lds + slot * SLOT + (i * 512 + wave * 64) * 16),
+                                             16, 0, 0);
+    };
+    v16f acc[MT32];
+#pragma unroll
+    for (int t = 0; t < MT32; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+
+    // B operand of token tile t, K step q: row 32 t + r32, chunk 2 q + h (the swizzle term
+    // depends on r32 only)
+    const int sw = (r32 >> 1) & 7;
+    int boff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) boff[q] = r32 * 128 + (((2 * q + h) ^ sw) << 4);
+
+    issue_w(0, 0);
+    issue_a(0, 0);
+    issue_w(1, 1);
+    for (int s0 = 0; s0 < nst; s0 += 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            // in flight in issue order: ... W(s) A(s) W(s+1): at most the 4 loads of
+            // W(s + 1) may still be outstanding
+            wait_vmcnt<4>();
+            lds_sync();  // everyone's A(s) landed; everyone is done reading A(s - 1)
+            issue_a(j ^ 1, s0 + j + 1);
+            __builtin_amdgcn_sched_barrier(0);  // keeps A(s+1) ahead of W(s+2) in issue order
+            const uint8_t* At = lds + j * SLOT;
+            bf16x8 bc[LOOK], bn[LOOK];
+#pragma unroll
+            for (int u = 0; u < LOOK; ++u) bc[u] = *(const bf16x8*)(At + boff[0] + u * 4096);
+#pragma unroll
+            for (int gq = 0; gq < 4 * NG; ++gq) {
+                const int q = gq / NG, tg = gq % NG;
+                if (gq + 1 < 4 * NG) {
+                    const int qn = (gq + 1) / NG, tn = (gq + 1) % NG;
+#pragma unroll
+                    for (int u = 0; u < LOOK; ++u)
+                        bn[u] = *(const bf16x8*)(At + boff[qn] + (tn * LOOK + u) * 4096);
+                }
+                bf16x8 wa;
+                __builtin_memcpy(&wa, &wf[j][q], 16);
+#pragma unroll
+                for (int u = 0; u < LOOK; ++u)
+                    acc[tg * LOOK + u] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bc[u], acc[tg * LOOK + u], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < LOOK; ++u) bc[u] = bn[u];
+            }
+            // the reads of group g + 1 go out before the MFMAs of group g
+            __builtin_amdgcn_sched_group_barrier(0x100, LOOK, 0);
+#pragma unroll
+            for (int gq = 0; gq < 4 * NG; ++gq) {
+                if (gq + 1 < 4 * NG) __builtin_amdgcn_sched_group_barrier(0x100, LOOK, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, LOOK, 0);
+            }
+            issue_w(j, s0 + j + 2);
+        }
+    }
+    wait_vmcnt<0>();  // no direct load may still target LDS when the workgroup ends
+    if (n0 >= a.N) return;
+    // D layout: lane holds token column r32 of the tile, rows 8 (v / 4) + 4 h + v % 4
+#pragma unroll
+    for (int t = 0; t < MT32; ++t) {
+        const int m = m0 + t * 32 + r32;
+        if (m >= a.M) continue;
+        float* dst = a.part + ((size_t)z * a.M + m) * a.N + n0 + 4 * h;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            *(v4f*)(dst + 8 * jj) = (v4f){acc[t][4 * jj], acc[t][4 * jj + 1], acc[t][4 * jj + 2],
+                                          acc[t][4 * jj + 3]};
+    }
+}
+
+// ---- plan ------------------------------------------------------------------------------
+// Split count from a cost model: the time is the larger of the MFMA time of the busiest
+// CU (rounds of workgroups) and the HBM time of the weights plus the split partials
+// (written, then read back by the reduce).  Rates are measured ones of this kernel on
+// MI355X: ~5 TFLOP/s per CU in its MFMA loop, ~5.5 TB/s of HBM traffic.
+struct WgPlan {
+    int S, NX, MCH, MT32;
+};
+
+static WgPlan wg_plan(int M, int N, int K) {
+    WgPlan p;
+    p.NX = (N + 255) / 256;
+    p.MCH = (M + 255) / 256;
+    const int mt = M < 256 ? M : 256;
+    p.MT32 = (mt + 31) / 32;
+    const int Q = K / 128;
+    const double cus = gemm_device_cus(), rate = 5.0e12, bw = 5.5e12;
+    const double wbytes = (double)N * K * 2 * p.MCH;
+    // the token count rounded up to its class (32-token steps, 256-token steps past 256):
+    // the plan is the same for every M of a class, so the class end bounds the partials
+    const double Mc = M <= 256 ? (double)p.MT32 * 32 : (double)p.MCH * 256;
+    double best = 1e30;
+    p.S = 1;
+    for (int S = 1; S <= Q && S <= 64; ++S) {
+        const double wgs = (double)p.NX * p.MCH * S;
+        const double rounds = (double)(long)((wgs + cus - 1) / cus);
+        const double kz = (double)((Q + S - 1) / S) * 128;  // the longest K range
+        const double t_mfma = rounds * 2.0 * 256 * (32.0 * p.MT32) * kz / rate;
+        const double t_hbm = (wbytes + 2.0 * S * Mc * N * 4) / bw;
+        const double t = t_mfma > t_hbm ? t_mfma : t_hbm;
+        if (t < best * 0.995) {
+            best = t;
+            p.S = S;
+        }
+    }
+    return p;
+}
+
+bool wgemm_fits(int N, int N0, int K, bool packed) {
+    if (K < 128 || K % 128 || N < 32 || N0 < 0 || N0 > N || N0 % 32 || (N - N0) % 32) return false;
+    if (packed && (N0 % 64 || (N - N0) % 64)) return false;
+    return true;
+}
+
+int wgemm_splits(int M, int N, int K) { return wg_plan(M, N, K).S; }
+
+size_t wgemm_parts_bytes(int M, int N, int K) {
+    // the plan depends on M through the 32-token tile count and the 256-token chunks:
+    // the largest M of each class bounds its partial buffer
+    size_t best = 0;
+    for (int m = 32;; m += (m < 256 ? 32 : 256)) {
+        const int mm = m < M ? m : M;
+        const size_t b = (size_t)wg_plan(mm, N, K).S * mm * N * sizeof(float);
+        if (b > best) best = b;
+        if (m >= M) break;
+    }
+    return best;
+}
+
+template <int MT32>
+static hipError_t launch_mt(const WgArgs& a, bool packed, int G, hipStream_t s) {
+    if (packed)
+        hipLaunchKernelGGL((k_wgemm<MT32, true>), dim3(G), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_wgemm<MT32, false>), dim3(G), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgemm(int M, int N, int N0, int K, const void* x, const void* w0,
+                        const void* w1, bool packed, float* parts, hipStream_t s, bool prio,
+                        int* S) {
+    const WgPlan p = wg_plan(M, N, K);
+    WgArgs a;
+    a.x = (const uint16_t*)x;
+    a.w0 = (const uint16_t*)w0;
+    a.w1 = (const uint16_t*)(w1 ? w1 : w0);
+    a.part = parts;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.N0 = N0;
+    a.S = p.S;
+    a.NX = p.NX;
+    a.MCH = p.MCH;
+    a.prio = prio ? 1 : 0;
+    *S = p.S;
+    const int G = p.NX * p.S * p.MCH;
+    switch (p.MT32) {
+        case 1: return launch_mt<1>(a, packed, G, s);
+        case 2: return launch_mt<2>(a, packed, G, s);
+        case 3: return launch_mt<3>(a, packed, G, s);
+        case 4: return launch_mt<4>(a, packed, G, s);
+        case 5: return launch_mt<5>(a, packed, G, s);
+        case 6: return launch_mt<6>(a, packed, G, s);
+        case 7: return launch_mt<7>(a, packed, G, s);
+        default: return launch_mt<8>(a, packed, G, s);
+    }
+}
+
+// ---- split reduce + epilogue -----------------------------------------------------------
+// Columns [0, N0) -> out0 as FP32 (the router logits of the front GEMM), columns [N0, N)
+// -> out1 (row stride N - N0) with MODE 0 FP32, 1 BF16 (one rounding), 2 BF16 of
+// FP32(add1) + sum.  Four columns per thread; the S partials are added in split order.
+template <int MODE>
+__device__ __forceinline__ void store4(void* out, const void* add, size_t idx, v4f v) {
+    if (MODE == 0) {
+        *(v4f*)((float*)out + idx) = v;
+    } else {
+        if (MODE == 2) {
+            const uint2 q = *(const uint2*)((const uint16_t*)add + idx);
+            v[0] += bf16_lo(q.x);
+            v[1] += bf16_hi(q.x);
+            v[2] += bf16_lo(q.y);
+            v[3] += bf16_hi(q.y);
+        }
+        *(uint2*)((uint16_t*)out + idx) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+}
+
+template <int MODE1>
+__global__ __launch_bounds__(256) void k_wg_reduce(int M, int N, int N0, int S,
+                                                   const float* __restrict__ part, float* out0,
+                                                   void* out1, const void* add1, int prio) {
+    if (prio) wave_priority_high();
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const int n4 = N / 4;
+    if (idx >= (long)M * n4) return;
+    const int m = (int)(idx / n4), c = (int)(idx - (long)m * n4) * 4;
+    const size_t zs = (size_t)M * N;
+    const float* p = part + (size_t)m * N + c;
+    v4f v = *(const v4f*)p;
+    for (int zz = 1; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
+    if (c < N0)
+        store4<0>(out0, nullptr, (size_t)m * N0 + c, v);
+    else
+        store4<MODE1>(out1, add1, (size_t)m * (N - N0) + (c - N0), v);
+}
+
+hipError_t launch_wg_reduce(int M, int N, int N0, int S, const float* parts, float* out0,
+                            int mode1, void* out1, const void* add1, hipStream_t s, bool prio) {
+    const long n = (long)M * (N / 4);
+    const dim3 grid((unsigned)((n + 255) / 256)), blk(256);
+    const int pr = prio ? 1 : 0;
+    if (mode1 == 0)
+        hipLaunchKernelGGL(k_wg_reduce<0>, grid, blk, 0, s, M, N, N0, S, parts, out0, out1, add1, pr);
+    else if (mode1 == 1)
+        hipLaunchKernelGGL(k_wg_reduce<1>, grid, blk, 0, s, M, N, N0, S, parts, out0, out1, add1, pr);
+    else
+        hipLaunchKernelGGL(k_wg_reduce<2>, grid, blk, 0, s, M, N, N0, S, parts, out0, out1, add1, pr);
+    return hipGetLastError();
+}
+
+// ---- packed dense layout ---------------------------------------------------------------
+// W [N, K] BF16 row-major -> blocks of 1 KiB: [N/64 row groups][K/64 K stages][tile 2]
+// [K step 4][lane 64][8 BF16], lane l of (group g, stage s, tile i, step q) holding row
+// 64 g + 32 i + l % 32, columns 64 s + 16 q + 8 (l / 32) .. + 8: the A operand of one
+// 32x32x16 MFMA.  A wavefront's loads for one K stage are 4 KiB in a row.
+__global__ __launch_bounds__(256) void k_pack_dense(int N, int K, const uint4* __restrict__ w,
+                                                    uint4* __restrict__ p) {
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte chunk
+    if (id >= (size_t)N * K / 8) return;
+    const int lane = (int)(id & 63), q = (int)((id >> 6) & 3), i = (int)((id >> 8) & 1);
+    const size_t rest = id >> 9;
+    const int ks = (int)(rest % (K / 64)), g = (int)(rest / (K / 64));
+    const int row = g * 64 + 32 * i + (lane & 31);
+    const int col = ks * 64 + 16 * q + 8 * (lane >> 5);
+    p[id] = w[((size_t)row * K + col) / 8];
+}
+
+hipError_t launch_pack_dense(int N, int K, const void* w, void* out, hipStream_t s) {
+    const size_t n = (size_t)N * K / 8;
+    hipLaunchKernelGGL(k_pack_dense, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, N, K,
+                       (const uint4*)w, (uint4*)out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

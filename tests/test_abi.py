@@ -155,6 +155,22 @@ def test_packed_format_and_pack_reject(L):
     assert L.moe_pack_expert_weights(None, C.byref(w), C.byref(w), None) == moe.MOE_ERR_NULL
 
 
+def test_dense_format_and_pack_dense_reject(L):
+    d = good_dims()
+    ew = moe.moe_expert_weights(FAKE, FAKE, FAKE, FAKE)
+    w = moe.moe_layer_weights(*([FAKE] * 7), ew, 5)
+    assert L.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, FAKE, 1 << 40, None) == moe.MOE_ERR_FORMAT
+    # packed dense weights need every matrix's rows in whole 64-row groups
+    d = good_dims(experts=96)
+    w = moe.moe_layer_weights(*([FAKE] * 7), ew, moe.MOE_DENSE_PACKED)
+    assert L.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, FAKE, 1 << 40, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_pack_dense_weight(32, 128, FAKE, FAKE + 4096, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_pack_dense_weight(64, 64, FAKE, FAKE + 4096, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_pack_dense_weight(64, 128, None, FAKE, None) == moe.MOE_ERR_NULL
+    assert L.moe_pack_dense_weight(64, 128, FAKE + 8, FAKE + (1 << 20), None) == moe.MOE_ERR_ALIGN
+    assert L.moe_pack_dense_weight(64, 128, FAKE, FAKE + 16, None) == moe.MOE_ERR_SHAPE  # overlap
+
+
 def test_linear_rmsnorm_silu_reject(L):
     assert L.moe_linear(8, 64, 100, FAKE, FAKE, FAKE, None, 1, None, 0, None) == moe.MOE_ERR_SHAPE
     assert L.moe_linear(8, 64, 128, FAKE, FAKE, FAKE, None, 5, None, 0, None) == moe.MOE_ERR_FORMAT

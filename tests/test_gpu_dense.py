@@ -35,6 +35,42 @@ def test_linear_small_int_exact(orc, M, N, K):
     assert np.array_equal(run_linear(x, w, 0), ref)
 
 
+# the weight-streaming path (K % 128 == 0, N % 32 == 0): one token, ragged 32-token tiles,
+# a second 256-token chunk that is partly empty, every token-tile count 1..8, split-K
+@pytest.mark.parametrize("M,N,K", [(1, 32, 128), (300, 224, 384), (510, 512, 1024),
+                                   (33, 4480, 7168), (97, 96, 256), (161, 64, 640),
+                                   (200, 320, 896), (230, 128, 2048)])
+def test_linear_streaming_small_int_exact(orc, M, N, K):
+    say(f"streaming linear M={M} N={N} K={K}")
+    g = np.random.default_rng(7 * M + N + K)
+    x = syn.small_int_bf16(g, (M, K), -2, 2)
+    w = syn.small_int_bf16(g, (N, K), -2, 2)
+    ref = (f32(x).astype(np.int64) @ f32(w).astype(np.int64).T).astype(np.float32)
+    assert np.array_equal(run_linear(x, w, 0), ref)
+
+
+def test_pack_dense_layout():
+    """moe_pack_dense_weight against the layout stated in the header, built here by
+    indexing: block (g, s, i, q), lane l, element e = W[64g + 32i + l%32, 64s + 16q + 8(l//32) + e]."""
+    N, K = 192, 384
+    g = np.random.default_rng(5)
+    w = g.integers(0, 1 << 16, size=(N, K), dtype=np.uint16)
+    got = host(moe.moe_pack_dense_weight(dev(w))).view(np.uint16).reshape(-1)
+    ref = np.empty(N * K, np.uint16)
+    at = 0
+    lane = np.arange(64)
+    for gi in range(N // 64):
+        for si in range(K // 64):
+            for i in range(2):
+                for q in range(4):
+                    rows = 64 * gi + 32 * i + lane % 32
+                    cols = 64 * si + 16 * q + 8 * (lane // 32)
+                    blk = w[rows[:, None], cols[:, None] + np.arange(8)[None, :]]
+                    ref[at:at + 512] = blk.reshape(-1)
+                    at += 512
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("M,N,K,mode", [(256, 3584, 7168, 1), (256, 7168, 6144, 1),
                                         (256, 7168, 3584, 2), (256, 12288, 7168, 1),
                                         (1020, 896, 7168, 0), (7, 72, 128, 2), (129, 200, 256, 0)])

@@ -20,10 +20,10 @@ from gpu_util import (assert_close, assert_close_bf16, bf16_ulp_dist, check_hidd
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(d, dw, x):
+def run_layer(d, dw, x, dense_format=moe.MOE_DENSE_ROWMAJOR):
     lw = moe.layer_weights(dw["w_gate"], dw["bias"], dw["w_down"], dw["w_shared_gu"],
                            dw["w_shared_dn"], dw["norm_w"], dw["w_up"], dw["w13"], dw["s13"],
-                           dw["w2"], dw["s2"])
+                           dw["w2"], dw["s2"], dense_format=dense_format)
     ws = torch.zeros(moe.moe_workspace_size(d), dtype=torch.uint8, device="cuda")
     out = torch.empty(d.tokens, d.hidden, dtype=torch.bfloat16, device="cuda")
     moe.moe_layer(d, lw, dev(x), out, ws)
@@ -113,3 +113,22 @@ def test_full_layer_packed_equals_row_major():
     dp = moe.dims(T, T, expert_format=moe.MOE_FMT_MXFP4_MXFP8_PACKED)
     out, _ = run_layer(dp, dwp, x)
     assert np.array_equal(out, out_ref)
+
+
+@pytest.mark.parametrize("T", [256, 65])
+def test_full_layer_dense_packed_equals_row_major(T):
+    """moe_layer on packed dense weights (moe_pack_dense_weight) gives the row-major
+    layer's output bit for bit; with the workspace intermediates equal too."""
+    w, dw = full_weights(0, False)
+    x = syn.layer_input(syn.full_dims(T), seed=2)
+    d = moe.dims(T, 1020)
+    say(f"dense packed vs row-major T={T}")
+    out_ref, ws_ref = run_layer(d, dw, x)
+    dwp = dict(dw)
+    for k in ("w_gate", "w_down", "w_shared_gu", "w_shared_dn", "w_up"):
+        dwp[k] = moe.moe_pack_dense_weight(dw[k])
+    out, ws = run_layer(d, dwp, x, dense_format=moe.MOE_DENSE_PACKED)
+    assert np.array_equal(out, out_ref)
+    v, vr = moe.workspace_views(d, ws), moe.workspace_views(d, ws_ref)
+    for k in ("logits", "latent", "shared"):
+        assert torch.equal(v[k], vr[k]), k

@@ -96,6 +96,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// 16-byte load marked non-temporal (the nt bit: the lines are streamed through the caches
+// with the lowest retention).  For weights that are read once per step: without it they
+// evict the small, re-read activations from L2 and those go back to HBM.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    const u32x4_nt v = __builtin_nontemporal_load((const u32x4_nt*)p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Raise this wavefront's issue priority (s_setprio 3).  The routing kernels are short and
 // latency-bound and run while the shared expert's GEMMs occupy every CU from another
 // stream; priority lets their waves issue first on a shared SIMD.  Stream priorities are

@@ -196,7 +196,7 @@ __device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
-            for (int i = 0; i < SPW; ++i) st.w[m][i] = *(const uint4*)(wb + (m * SPW + i) * 1024);
+            for (int i = 0; i < SPW; ++i) st.w[m][i] = load_stream16(wb + (m * SPW + i) * 1024);
             load_dwords<SPW>(sbase + (m * 16 + r16) * (4 * SPW), st.ws[m]);
         }
         return;
@@ -207,7 +207,7 @@ __device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int
         const size_t R = ebase + (m >> 1) * I + st.j * UP_COLS + (m & 1) * 16 + r16;
         const uint8_t* base = w13 + R * (L / 2) + (SPW * wave) * 64 + 16 * g;
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) st.w[m][i] = *(const uint4*)(base + i * 64);
+        for (int i = 0; i < SPW; ++i) st.w[m][i] = load_stream16(base + i * 64);
         load_dwords<SPW>(s13 + R * SROW + 4 * SPW * wave, st.ws[m]);
     }
 }
@@ -475,8 +475,8 @@ __device__ __forceinline__ void down_issue_weights(DownStage<IS, MT>& st, int it
         const size_t R = R0 + m * 16;
 #pragma unroll
         for (int s = 0; s < IS; ++s)
-            st.w[m][s] = PACKED ? *(const uint4*)(wb + (m * IS + s) * 1024)
-                                : *(const uint4*)(w2 + R * WROW + s * 64 + 16 * g);
+            st.w[m][s] = PACKED ? load_stream16(wb + (m * IS + s) * 1024)
+                                : load_stream16(w2 + R * WROW + s * 64 + 16 * g);
         load_dwords<IS>(s2 + R * SROW, st.sw[m]);
     }
 }

@@ -92,8 +92,8 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
         const int k0 = kb + min(st, nst - 1) * 64;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            wf[slot][q] = *(const uint4*)(PACKED ? wsrc + (size_t)(k0 / 64) * 4096 + q * 512
-                                                 : wsrc + k0 + 16 * q);
+            wf[slot][q] = load_stream16(PACKED ? wsrc + (size_t)(k0 / 64) * 4096 + q * 512
+                                               : wsrc + k0 + 16 * q);
     };
     auto issue_a = [&](int slot, int st) {
         const int k0 = kb + min(st, nst - 1) * 64;

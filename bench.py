@@ -65,8 +65,10 @@ def recorded_traffic(T, zipf, row_major):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    # the GPU lowers its clocks when idle and takes some 0.1 s of load to reach them
+    # again: the default warmup (~0.2 s of layers) measures the steady state
+    p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--tokens", type=int, default=256)
     p.add_argument("--zipf", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,7 +165,7 @@ def main():
         def call():
             moe.moe_grouped_ffn_stages(*ffn_w, v["codes"], v["scales"], *lists, rows, fws,
                                        stages, stream=stream)
-        for _ in range(3):
+        for _ in range(max(a.warmup // 2, 3)):  # back to steady-state clocks after the host work
             call()
         torch.cuda.synchronize()
         f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

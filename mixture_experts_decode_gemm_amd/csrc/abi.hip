@@ -51,7 +51,7 @@ moe_status check_dims(const moe_dims* d) {
 
 struct Layout {
     size_t off[MOE_WS_FIELDS];
-    size_t gu, act, uni, uni_side, total;
+    size_t gu, act, uni, uni_side, parts, total;
 };
 
 Layout layout(const moe_dims* d) {
@@ -73,17 +73,15 @@ Layout layout(const moe_dims* d) {
     at += up256(T * 2 * S * 2);
     lo.act = at;
     at += up256(T * S * 2);
-    lo.uni = at;
+    // scratch of the routed path (list bitmaps; the tiled GEMMs' split partials), of the
+    // shared expert's GEMMs on the side stream (their split partials), and the partials of
+    // the front GEMM (router + latent down), later of the up-projection
     const int Tm = d->max_tokens;
-    // scratch of the routed path (router, latent down and up GEMMs, list bitmaps) and,
-    // apart from it, of the shared expert's GEMMs, which run concurrently on a side stream
-    // (the sizes of both dense paths: the weight-streaming GEMM where the shapes allow it,
-    // the tiled GEMM otherwise)
     const int Hi = d->hidden, Li = d->latent, Ei = d->experts, S2 = 2 * d->shared_inter;
+    lo.uni = at;
     size_t u = 0;
-    const size_t g[6] = {gemm_scratch_bytes(Tm, Ei, Hi),      gemm_scratch_bytes(Tm, Li, Hi),
-                         gemm_scratch_bytes(Tm, Hi, Li),      wgemm_parts_bytes(Tm, Ei + Li, Hi),
-                         wgemm_parts_bytes(Tm, Hi, Li),       lists_scratch_bytes(Tm, Ei)};
+    const size_t g[4] = {gemm_scratch_bytes(Tm, Ei, Hi), gemm_scratch_bytes(Tm, Li, Hi),
+                         gemm_scratch_bytes(Tm, Hi, Li), lists_scratch_bytes(Tm, Ei)};
     for (size_t v : g) u = v > u ? v : u;
     at += up256(u);
     lo.uni_side = at;
@@ -92,6 +90,9 @@ Layout layout(const moe_dims* d) {
                           wgemm_parts_bytes(Tm, S2, Hi), wgemm_parts_bytes(Tm, Hi, d->shared_inter)};
     for (size_t v : g2) us = v > us ? v : us;
     at += up256(us);
+    lo.parts = at;
+    const size_t p1 = wgemm_parts_bytes(Tm, Ei + Li, Hi), p2 = wgemm_parts_bytes(Tm, Hi, Li);
+    at += up256(p1 > p2 ? p1 : p2);
     lo.total = at;
     return lo;
 }
@@ -129,7 +130,9 @@ extern "C" {
 const char* moe_version(void) { return "libmoedecode 0.1 (gfx950)"; }
 
 // the router GEMM: the weight-streaming kernel when the shape allows it
-bool router_fast(const moe_dims* d) { return wgemm_fits(d->experts, d->experts, d->hidden, false); }
+bool router_fast(const moe_dims* d) {
+    return wgemm_fits(d->max_tokens, d->experts, d->experts, d->experts, d->hidden, false);
+}
 
 size_t router_scratch(const moe_dims* d, int M) {
     return router_fast(d) ? wgemm_parts_bytes(M, d->experts, d->hidden)
@@ -158,10 +161,11 @@ moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
     hipStream_t s = (hipStream_t)stream;
     if (!given && router_fast(d)) {
         int S = 1;
-        if (launch_wgemm(d->tokens, d->experts, d->experts, d->hidden, x, w_gate, nullptr, false,
-                         (float*)workspace, s, false, &S) != hipSuccess ||
-            launch_wg_reduce(d->tokens, d->experts, d->experts, S, (const float*)workspace, logits,
-                             0, nullptr, nullptr, s, false) != hipSuccess)
+        if (launch_wgemm(d->tokens, d->experts, d->experts, d->experts, d->hidden, x, w_gate,
+                         nullptr, nullptr, false, (float*)workspace, s, false, &S) != hipSuccess ||
+            launch_wg_reduce(d->tokens, d->experts, d->experts, d->experts, S,
+                             (const float*)workspace, logits, 0, nullptr, nullptr, s,
+                             false) != hipSuccess)
             return MOE_ERR_LAUNCH;
     } else if (!given) {
         hipError_t e = launch_gemm(d->tokens, d->experts, d->hidden, x, w_gate, logits, nullptr, 0,
@@ -294,7 +298,8 @@ moe_status moe_rmsnorm(int32_t rows, int32_t cols, const void* r, const void* g,
 
 size_t moe_linear_workspace_size(int32_t M, int32_t N, int32_t K) {
     if (M < 1 || N < 1 || K < 64 || K % 64) return 0;
-    return wgemm_fits(N, N, K, false) ? wgemm_parts_bytes(M, N, K) : gemm_scratch_bytes(M, N, K);
+    return wgemm_fits(M, N, N, N, K, false) ? wgemm_parts_bytes(M, N, K)
+                                            : gemm_scratch_bytes(M, N, K);
 }
 
 moe_status moe_linear(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* out,
@@ -304,17 +309,17 @@ moe_status moe_linear(int32_t M, int32_t N, int32_t K, const void* x, const void
     if (mode < MOE_LINEAR_F32 || mode > MOE_LINEAR_ADD_BF16) return MOE_ERR_FORMAT;
     if (!x || !w || !out || (mode == MOE_LINEAR_ADD_BF16 && !add)) return MOE_ERR_NULL;
     if (!al16(x) || !al16(w) || !al16(out) || (add && !al16(add))) return MOE_ERR_ALIGN;
-    const bool fast = wgemm_fits(N, N, K, false);
+    const bool fast = wgemm_fits(M, N, N, N, K, false);
     const size_t need = fast ? wgemm_parts_bytes(M, N, K) : gemm_scratch_bytes(M, N, K);
     if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
     if (workspace && !al16(workspace)) return MOE_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     if (fast) {
         int S = 1;
-        if (launch_wgemm(M, N, N, K, x, w, nullptr, false, (float*)workspace, s, false, &S) !=
-            hipSuccess)
+        if (launch_wgemm(M, N, N, N, K, x, w, nullptr, nullptr, false, (float*)workspace, s, false,
+                         &S) != hipSuccess)
             return MOE_ERR_LAUNCH;
-        return launch_status(launch_wg_reduce(M, N, 0, S, (const float*)workspace, nullptr, mode,
+        return launch_status(launch_wg_reduce(M, N, 0, N, S, (const float*)workspace, nullptr, mode,
                                               out, add, s, false));
     }
     return launch_status(launch_gemm(M, N, K, x, w, out, add, mode, workspace, s));
@@ -372,10 +377,12 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     // the weight-streaming GEMMs for every dense projection, else (row-major weights of
     // shapes they do not take) the tiled GEMM
     const int S2 = 2 * d->shared_inter;
-    const bool fast = wgemm_fits(d->experts + d->latent, d->experts, d->hidden, dpack) &&
-                      wgemm_fits(S2, S2, d->hidden, dpack) &&
-                      wgemm_fits(d->hidden, d->hidden, d->shared_inter, dpack) &&
-                      wgemm_fits(d->hidden, d->hidden, d->latent, dpack);
+    const int H_ = d->hidden, L_ = d->latent;
+    const int Tm = d->max_tokens;
+    const bool fast = wgemm_fits(Tm, d->experts + L_, d->experts, d->experts + L_, H_, dpack) &&
+                      wgemm_fits(Tm, S2, S2, S2, H_, dpack) &&
+                      wgemm_fits(Tm, H_, H_, H_, d->shared_inter, dpack) &&
+                      wgemm_fits(Tm, H_, H_, H_, L_, dpack);
     if (dpack && !fast) return MOE_ERR_SHAPE;
     const Layout lo = layout(d);
     if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE;
@@ -410,45 +417,52 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     do {                                                \
         if ((call) != hipSuccess) return MOE_ERR_LAUNCH; \
     } while (0)
-    // The shared expert depends on x only: it runs on the side stream ([wide] module
-    // summary and [ep] module summary: the shared expert on a side stream beside the
-    // routed experts), joined before the up-projection adds into its output.  Without a
-    // side stream it runs in order on `s`.
     SideStream* ss = side_stream();
     std::unique_lock<std::mutex> side_lock;
     if (ss) side_lock = std::unique_lock<std::mutex>(ss->mu);
     hipStream_t sh = ss ? ss->s : s;
-    if (ss) {
-        MOE_TRY(hipEventRecord(ss->fork, s));
-        MOE_TRY(hipStreamWaitEvent(sh, ss->fork, 0));
-    }
-    // gate/up as split-K partials; the activation adds them and rounds (the gate/up BF16
-    // values) before SiLU-and-mul
-    int s_gu = 1, s_sd = 1, s_fr = 1, s_up = 1;
+    int s_fr = 1, s_gu = 1, s_sd = 1, s_up = 1;
+    float* parts = (float*)(ws + lo.parts);
     float* parts_side = (float*)uni_side;
-    float* parts = (float*)uni;
     if (fast) {
-        MOE_TRY(launch_wgemm(T, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, dpack, parts_side, sh,
-                             false, &s_gu));
-        MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, act, sh));
-        MOE_TRY(launch_wgemm(T, H, H, S, act, w->w_shared_down, nullptr, dpack, parts_side, sh,
-                             false, &s_sd));
-        MOE_TRY(launch_wg_reduce(T, H, 0, s_sd, parts_side, nullptr, 1, shared, nullptr, sh, false));
+        // The shared expert depends on x only: its gate/up GEMM, activation, down GEMM and
+        // rounding run on the side stream ([wide] and [ep] module summaries: the shared
+        // expert beside the routed path), joined before the up-projection adds into it.
+        if (ss) {
+            MOE_TRY(hipEventRecord(ss->fork, s));
+            MOE_TRY(hipStreamWaitEvent(sh, ss->fork, 0));
+        }
+        MOE_TRY(launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr, dpack,
+                             parts_side, sh, false, &s_gu));
+        MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh));
+        MOE_TRY(launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
+                             parts_side, sh, false, &s_sd));
+        MOE_TRY(launch_wg_reduce(T, H, 0, H, s_sd, parts_side, nullptr, 1, shared, nullptr, sh,
+                                 false));
+        if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
+        // [wide] front: the router rows and the latent down rows as one FP32-out GEMM over
+        // x; FP32 logits and the latent rounded once to BF16 from the same partials
+        MOE_TRY(launch_wgemm(T, E + L, E, E + L, H, x, w->w_gate, w->w_down, nullptr, dpack, parts,
+                             s, true, &s_fr));
+        MOE_TRY(launch_wg_reduce(T, E + L, E, E + L, s_fr, parts, logits, 1, latent, nullptr, s,
+                                 true));
     } else {
+        // The shared expert depends on x only: it runs on the side stream beside the whole
+        // routed path; gate/up as split-K partials, whose sum the activation rounds (the
+        // gate/up BF16 values) before SiLU-and-mul
+        if (ss) {
+            MOE_TRY(hipEventRecord(ss->fork, s));
+            MOE_TRY(hipStreamWaitEvent(sh, ss->fork, 0));
+        }
         MOE_TRY(launch_gemm_parts(T, 2 * S, H, x, w->w_shared_gu, parts_side, sh, false, &s_gu));
-        MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, act, sh));
+        MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh));
         MOE_TRY(launch_gemm(T, H, S, act, w->w_shared_down, shared, nullptr, 1, uni_side, sh));
-    }
-    if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
-    // routing: FP32 router GEMM (with the latent down in one GEMM over x: FP32 logits and
-    // the latent rounded once to BF16), sigmoid top-K, lists and unit windows
-    if (fast) {
-        MOE_TRY(launch_wgemm(T, E + L, E, H, x, w->w_gate, w->w_down, dpack, parts, s, true, &s_fr));
-        MOE_TRY(launch_wg_reduce(T, E + L, E, s_fr, parts, logits, 1, latent, nullptr, s, true));
-    } else {
+        if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
+        // routing: FP32 router GEMM, the latent down GEMM (one BF16 rounding)
         MOE_TRY(launch_gemm(T, E, H, x, w->w_gate, logits, nullptr, 0, uni, s, 0, true));
         MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s, 0, true));
     }
+    // sigmoid top-K, lists and unit windows
     MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts, s));
     MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, s));
     // MXFP8 latent, grouped experts, Finalize
@@ -467,8 +481,9 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     // the up-projection added into the shared partial (one rounding)
     if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
     if (fast) {
-        MOE_TRY(launch_wgemm(T, H, H, L, normed, w->w_up, nullptr, dpack, parts, s, false, &s_up));
-        MOE_TRY(launch_wg_reduce(T, H, 0, s_up, parts, nullptr, 2, out, shared, s, false));
+        MOE_TRY(launch_wgemm(T, H, H, H, L, normed, w->w_up, nullptr, nullptr, dpack, parts, s,
+                             false, &s_up));
+        MOE_TRY(launch_wg_reduce(T, H, 0, H, s_up, parts, nullptr, 2, out, shared, s, false));
     } else {
         MOE_TRY(launch_gemm(T, H, L, normed, w->w_up, out, shared, 2, uni, s));
     }

@@ -56,22 +56,25 @@ int gemm_splits(int M, int N, int K);
 size_t gemm_parts_bytes(int M, int N, int K);
 hipError_t launch_gemm_parts(int M, int N, int K, const void* x, const void* w, float* parts,
                              hipStream_t s, bool prio, int* S);
-hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, void* out,
+// SiLU-and-mul of the gate/up GEMM's split partials: gate columns [0, S) and up columns
+// [S, 2S) of rows with stride ld floats, nsplit slabs of M rows
+hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, int ld, void* out,
                                  hipStream_t s);
 
-// weight-streaming dense GEMM (wgemm.hip): FP32 split partials [S][M][N] of x W^T where
-// rows [0, N0) of W come from w0 and rows [N0, N) from w1 (row-major, or packed by
-// launch_pack_dense); *S receives the split count.  wgemm_fits tells whether the shape is
-// supported (K % 128 == 0, N0 and N - N0 multiples of 32, of 64 when packed).
-bool wgemm_fits(int N, int N0, int K, bool packed);
+// weight-streaming dense GEMM (wgemm.hip): FP32 split partials [S][M][N] of x W^T where W
+// is three row segments stacked: rows [0, N0) from w0, [N0, N1) from w1, [N1, N) from w2
+// (row-major, or packed by launch_pack_dense; empty segments may pass null); *S receives
+// the split count.  wgemm_fits tells whether the shape is supported (K % 128 == 0, every
+// segment a multiple of 32 rows, of 64 when packed, M * K < 2^31).
+bool wgemm_fits(int M, int N, int N0, int N1, int K, bool packed);
 int wgemm_splits(int M, int N, int K);
 size_t wgemm_parts_bytes(int M, int N, int K);
-hipError_t launch_wgemm(int M, int N, int N0, int K, const void* x, const void* w0,
-                        const void* w1, bool packed, float* parts, hipStream_t s, bool prio,
-                        int* S);
-// adds the S partials in split order: columns [0, N0) to out0 (FP32), the rest to out1 with
-// mode1 0 FP32, 1 BF16, 2 BF16 of add1 + sum
-hipError_t launch_wg_reduce(int M, int N, int N0, int S, const float* parts, float* out0,
+hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
+                        const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
+                        bool prio, int* S);
+// adds the S partials (rows of stride N) in split order: columns [0, N0) to out0 (FP32),
+// [N0, N1) to out1 with mode1 0 FP32, 1 BF16, 2 BF16 of add1 + sum; columns past N1 untouched
+hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* parts, float* out0,
                             int mode1, void* out1, const void* add1, hipStream_t s, bool prio);
 // W [N, K] BF16 -> the packed layout (N % 64 == 0, K % 64 == 0)
 hipError_t launch_pack_dense(int N, int K, const void* w, void* out, hipStream_t s);

@@ -71,18 +71,18 @@ __global__ __launch_bounds__(256) void k_silu_mul(int M, int S8, const uint4* __
     out[gid] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// The same from the gate/up GEMM's nsplit FP32 split-K partials [nsplit][M][2S]: each
-// gate and up value is the split-order sum rounded once to BF16 (the GEMM's output), then
-// as above.
-__global__ __launch_bounds__(256) void k_silu_mul_parts(int M, int S8, int nsplit,
+// The same from the gate/up GEMM's nsplit FP32 split-K partials: slab z holds M rows of
+// stride ld floats, gate values in columns [0, S), up values in [S, 2S).  Each gate and up
+// value is the split-order sum rounded once to BF16 (the GEMM's output), then as above.
+__global__ __launch_bounds__(256) void k_silu_mul_parts(int M, int S8, int nsplit, int ld4,
                                                         const float4* __restrict__ parts,
                                                         uint4* __restrict__ out) {
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
     if (gid >= (long)M * S8) return;
     const long m = gid / S8, c = gid - m * S8;
-    const long zs = (long)M * S8 * 4;                  // float4s per split (M x 2S floats)
-    const float4* gp = parts + m * S8 * 4 + c * 2;     // 8 gate floats of this thread
-    const float4* up = gp + S8 * 2;                    // 8 up floats
+    const long zs = (long)M * ld4;                  // float4s per split
+    const float4* gp = parts + m * ld4 + c * 2;     // 8 gate floats of this thread
+    const float4* up = gp + S8 * 2;                 // 8 up floats
     float gv[8], uv[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -107,11 +107,11 @@ __global__ __launch_bounds__(256) void k_silu_mul_parts(int M, int S8, int nspli
     out[gid] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, void* out,
+hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, int ld, void* out,
                                  hipStream_t s) {
     const long n = (long)M * (S / 8);
     hipLaunchKernelGGL(k_silu_mul_parts, dim3((int)((n + 255) / 256)), dim3(256), 0, s, M, S / 8,
-                       nsplit, (const float4*)parts, (uint4*)out);
+                       nsplit, ld / 4, (const float4*)parts, (uint4*)out);
     return hipGetLastError();
 }
 

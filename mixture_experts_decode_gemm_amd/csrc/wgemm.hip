@@ -41,22 +41,31 @@ __device__ __forceinline__ int wg_xcd_item(int b, int G) {
 }
 
 struct WgArgs {
-    const uint16_t* x;   // [M, K] BF16
-    const uint16_t* w0;  // rows [0, N0): row-major [N0, K] or packed
-    const uint16_t* w1;  // rows [N0, N): row-major [N - N0, K] or packed (may be null if N0 == N)
-    float* part;         // [S][M][N] FP32
-    int M, K, N, N0, S, NX, MCH, prio;
+    const uint16_t* x;     // [M, K] BF16
+    const uint16_t* w[3];  // row segments [0, N0), [N0, N1), [N1, N): row-major or packed
+    float* part;           // [S][M][N] FP32
+    int M, K, N, N0, N1, S, NX, MCH, prio;
 };
 
-// MT32: 32-token tiles computed per token chunk (1..8); PACKED: weights in the packed
-// layout of launch_pack_dense.
-template <int MT32, bool PACKED>
+// MT32: 32-token tiles computed per token chunk (1..8); KS: K depth of one LDS stage (64
+// or 128); PACKED: weights in the packed layout of launch_pack_dense.
+template <int MT32, int KS, bool PACKED>
 __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
-    constexpr int ROWS = (MT32 + 1) / 2 * 64;  // token rows staged (whole direct-load rounds)
-    constexpr int LA = ROWS / 64;              // direct loads per thread per K stage
-    constexpr int SLOT = ROWS * 128;           // bytes of one LDS stage (64 K x ROWS)
-    constexpr int LOOK = MT32 % 4 == 0 ? 4 : (MT32 % 3 == 0 ? 3 : (MT32 % 2 == 0 ? 2 : MT32));
-    constexpr int NG = MT32 / LOOK;  // LDS read groups per 16-deep K step
+    constexpr int CPR = KS / 8;   // 16-byte chunks of one token row of a stage
+    constexpr int RB = KS * 2;    // bytes of one token row of a stage
+    // token rows staged: whole rounds of direct loads (512 threads x 16 bytes)
+    constexpr int ROWS = KS == 64 ? (MT32 + 1) / 2 * 64 : MT32 * 32;
+    constexpr int LA = ROWS * CPR / 512;  // direct loads per thread per stage
+    constexpr int SLOT = ROWS * RB;       // bytes of one LDS stage
+    constexpr int NQ = KS / 16;           // MFMA K steps per stage
+    constexpr int TSTR = 32 * RB;         // bytes between 32-token tiles in a stage
+    // LDS fragments read ahead per group (a divisor of MT32; smaller where the registers of
+    // 128-deep stages run short)
+    constexpr int LOOK = (KS == 128 && MT32 >= 7)
+                             ? (MT32 == 8 ? 2 : 1)
+                             : (MT32 % 4 == 0 ? 4 : (MT32 % 3 == 0 ? 3 : (MT32 % 2 == 0 ? 2 : MT32)));
+    constexpr int NG = MT32 / LOOK;  // LDS read groups per K step
+    static_assert(LA * 512 == ROWS * CPR, "direct-load rounds");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
     if (a.prio) wave_priority_high();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -64,42 +73,47 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
     const int item = wg_xcd_item(blockIdx.x, a.NX * a.S * a.MCH);
     const int nt = item % a.NX, rest = item / a.NX;
     const int z = rest % a.S, mc = rest / a.S;
-    const int Q = a.K / 128;  // K in pairs of stages
+    const int Q = a.K / (2 * KS);  // K in pairs of stages
     const int q0 = z * Q / a.S, q1 = (z + 1) * Q / a.S;
-    const int kb = q0 * 128, nst = (q1 - q0) * 2;
+    const int kb = q0 * 2 * KS, nst = (q1 - q0) * 2;
     const int n0 = nt * 256 + wave * 32;  // this wavefront's 32 output rows
     const int m0 = mc * 256;
 
     // weight rows of this wavefront (past N: a valid tile, loaded but never stored)
     const int nrow = min(n0, a.N - 32);
-    const bool second = nrow >= a.N0;
-    const uint16_t* wm = second ? a.w1 : a.w0;
-    const int wr = second ? nrow - a.N0 : nrow;
+    const int seg = nrow >= a.N1 ? 2 : (nrow >= a.N0 ? 1 : 0);
+    const int wr = nrow - (seg == 2 ? a.N1 : (seg == 1 ? a.N0 : 0));
+    const uint16_t* wm = a.w[seg];
     const uint16_t* wsrc =
         PACKED ? wm + (size_t)(wr / 64) * (a.K / 64) * 4096 + ((wr % 64) / 32) * 2048 + lane * 8
                : wm + (size_t)(wr + r32) * a.K + 8 * h;
-    // activation chunks: LDS chunk p = i * 512 + tid holds row p / 8, chunk (p % 8) ^ sw(row)
-    const uint16_t* asrc[LA];
+    // Activation stage layout: token row r at r * RB, its 16-byte chunk c at position
+    // c ^ sw(r), sw(r) = ((r >> 1) & 7) for 128-byte rows, (r & 15) for 256-byte rows, so
+    // that the fragment reads of 16 consecutive rows hit 16 distinct bank groups.  The
+    // direct loads fill LDS chunk p = i * 512 + tid with the global chunk that belongs there.
+    uint32_t asrc[LA];  // element offsets into x (M * K < 2^31)
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int p = i * 512 + tid, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-        asrc[i] = a.x + (size_t)min(m0 + r, a.M - 1) * a.K + 8 * c;
+        const int p = i * 512 + tid, r = p / CPR;
+        const int c = (p % CPR) ^ (KS == 64 ? ((r >> 1) & 7) : (r & 15));
+        asrc[i] = (uint32_t)(min(m0 + r, a.M - 1) * a.K + 8 * c);
     }
     // stages past the end repeat the last one (never used), so every thread always has
     // the same loads in flight
-    uint4 wf[2][4];
+    uint4 wf[2][NQ];
     auto issue_w = [&](int slot, int st) {
-        const int k0 = kb + min(st, nst - 1) * 64;
+        const int k0 = kb + min(st, nst - 1) * KS;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            wf[slot][q] = load_stream16(PACKED ? wsrc + (size_t)(k0 / 64) * 4096 + q * 512
-                                               : wsrc + k0 + 16 * q);
+        for (int q = 0; q < NQ; ++q)
+            wf[slot][q] = load_stream16(
+                PACKED ? wsrc + (size_t)(k0 / 64 + q / 4) * 4096 + (q % 4) * 512
+                       : wsrc + k0 + 16 * q);
     };
     auto issue_a = [&](int slot, int st) {
-        const int k0 = kb + min(st, nst - 1) * 64;
+        const int k0 = kb + min(st, nst - 1) * KS;
 #pragma unroll
         for (int i = 0; i < LA; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + k0),
+            __builtin_amdgcn_global_load_lds((const void*)(a.x + asrc[i] + k0),
                                              (lds_ptr)(lds + slot * SLOT + (i * 512 + wave * 64) * 16),
                                              16, 0, 0);
     };
@@ -111,10 +125,10 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
 
     // B operand of token tile t, K step q: row 32 t + r32, chunk 2 q + h (the swizzle term
     // depends on r32 only)
-    const int sw = (r32 >> 1) & 7;
-    int boff[4];
+    const int sw = KS == 64 ? ((r32 >> 1) & 7) : (r32 & 15);
+    int boff[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) boff[q] = r32 * 128 + (((2 * q + h) ^ sw) << 4);
+    for (int q = 0; q < NQ; ++q) boff[q] = r32 * RB + (((2 * q + h) ^ sw) << 4);
 
     issue_w(0, 0);
     issue_a(0, 0);
@@ -122,24 +136,24 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
     for (int s0 = 0; s0 < nst; s0 += 2) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            // in flight in issue order: ... W(s) A(s) W(s+1): at most the 4 loads of
+            // in flight in issue order: ... W(s) A(s) W(s+1): at most the NQ loads of
             // W(s + 1) may still be outstanding
-            wait_vmcnt<4>();
+            wait_vmcnt<NQ>();
             lds_sync();  // everyone's A(s) landed; everyone is done reading A(s - 1)
             issue_a(j ^ 1, s0 + j + 1);
             __builtin_amdgcn_sched_barrier(0);  // keeps A(s+1) ahead of W(s+2) in issue order
             const uint8_t* At = lds + j * SLOT;
             bf16x8 bc[LOOK], bn[LOOK];
 #pragma unroll
-            for (int u = 0; u < LOOK; ++u) bc[u] = *(const bf16x8*)(At + boff[0] + u * 4096);
+            for (int u = 0; u < LOOK; ++u) bc[u] = *(const bf16x8*)(At + boff[0] + u * TSTR);
 #pragma unroll
-            for (int gq = 0; gq < 4 * NG; ++gq) {
+            for (int gq = 0; gq < NQ * NG; ++gq) {
                 const int q = gq / NG, tg = gq % NG;
-                if (gq + 1 < 4 * NG) {
+                if (gq + 1 < NQ * NG) {
                     const int qn = (gq + 1) / NG, tn = (gq + 1) % NG;
 #pragma unroll
                     for (int u = 0; u < LOOK; ++u)
-                        bn[u] = *(const bf16x8*)(At + boff[qn] + (tn * LOOK + u) * 4096);
+                        bn[u] = *(const bf16x8*)(At + boff[qn] + (tn * LOOK + u) * TSTR);
                 }
                 bf16x8 wa;
                 __builtin_memcpy(&wa, &wf[j][q], 16);
@@ -153,8 +167,8 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
             // the reads of group g + 1 go out before the MFMAs of group g
             __builtin_amdgcn_sched_group_barrier(0x100, LOOK, 0);
 #pragma unroll
-            for (int gq = 0; gq < 4 * NG; ++gq) {
-                if (gq + 1 < 4 * NG) __builtin_amdgcn_sched_group_barrier(0x100, LOOK, 0);
+            for (int gq = 0; gq < NQ * NG; ++gq) {
+                if (gq + 1 < NQ * NG) __builtin_amdgcn_sched_group_barrier(0x100, LOOK, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, LOOK, 0);
             }
             issue_w(j, s0 + j + 2);
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
 // (written, then read back by the reduce).  Rates are measured ones of this kernel on
 // MI355X: ~5 TFLOP/s per CU in its MFMA loop, ~5.5 TB/s of HBM traffic.
 struct WgPlan {
-    int S, NX, MCH, MT32;
+    int S, NX, MCH, MT32, KS;
 };
 
 static WgPlan wg_plan(int M, int N, int K) {
@@ -190,7 +204,8 @@ static WgPlan wg_plan(int M, int N, int K) {
     p.MCH = (M + 255) / 256;
     const int mt = M < 256 ? M : 256;
     p.MT32 = (mt + 31) / 32;
-    const int Q = K / 128;
+    p.KS = 64;  // (128-deep stages measured no faster at the layer's shapes)
+    const int Q = K / (2 * p.KS);
     const double cus = gemm_device_cus(), rate = 5.0e12, bw = 5.5e12;
     const double wbytes = (double)N * K * 2 * p.MCH;
     // the token count rounded up to its class (32-token steps, 256-token steps past 256):
@@ -201,7 +216,7 @@ static WgPlan wg_plan(int M, int N, int K) {
     for (int S = 1; S <= Q && S <= 64; ++S) {
         const double wgs = (double)p.NX * p.MCH * S;
         const double rounds = (double)(long)((wgs + cus - 1) / cus);
-        const double kz = (double)((Q + S - 1) / S) * 128;  // the longest K range
+        const double kz = (double)((Q + S - 1) / S) * 2 * p.KS;  // the longest K range
         const double t_mfma = rounds * 2.0 * 256 * (32.0 * p.MT32) * kz / rate;
         const double t_hbm = (wbytes + 2.0 * S * Mc * N * 4) / bw;
         const double t = t_mfma > t_hbm ? t_mfma : t_hbm;
@@ -213,10 +228,11 @@ static WgPlan wg_plan(int M, int N, int K) {
     return p;
 }
 
-bool wgemm_fits(int N, int N0, int K, bool packed) {
-    if (K < 128 || K % 128 || N < 32 || N0 < 0 || N0 > N || N0 % 32 || (N - N0) % 32) return false;
-    if (packed && (N0 % 64 || (N - N0) % 64)) return false;
-    return true;
+bool wgemm_fits(int M, int N, int N0, int N1, int K, bool packed) {
+    const int q = packed ? 64 : 32;
+    if (K < 128 || K % 128 || N < 32 || N0 < 0 || N1 < N0 || N1 > N) return false;
+    if (M < 1 || (long)M * K >= (1L << 31)) return false;  // 32-bit activation offsets
+    return N0 % q == 0 && (N1 - N0) % q == 0 && (N - N1) % q == 0;
 }
 
 int wgemm_splits(int M, int N, int K) { return wg_plan(M, N, K).S; }
@@ -234,50 +250,58 @@ size_t wgemm_parts_bytes(int M, int N, int K) {
     return best;
 }
 
-template <int MT32>
+template <int MT32, int KS>
 static hipError_t launch_mt(const WgArgs& a, bool packed, int G, hipStream_t s) {
     if (packed)
-        hipLaunchKernelGGL((k_wgemm<MT32, true>), dim3(G), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_wgemm<MT32, KS, true>), dim3(G), dim3(512), 0, s, a);
     else
-        hipLaunchKernelGGL((k_wgemm<MT32, false>), dim3(G), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_wgemm<MT32, KS, false>), dim3(G), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_wgemm(int M, int N, int N0, int K, const void* x, const void* w0,
-                        const void* w1, bool packed, float* parts, hipStream_t s, bool prio,
-                        int* S) {
+template <int KS>
+static hipError_t launch_ks(const WgArgs& a, int mt32, bool packed, int G, hipStream_t s) {
+    switch (mt32) {
+        case 1: return launch_mt<1, KS>(a, packed, G, s);
+        case 2: return launch_mt<2, KS>(a, packed, G, s);
+        case 3: return launch_mt<3, KS>(a, packed, G, s);
+        case 4: return launch_mt<4, KS>(a, packed, G, s);
+        case 5: return launch_mt<5, KS>(a, packed, G, s);
+        case 6: return launch_mt<6, KS>(a, packed, G, s);
+        case 7: return launch_mt<7, KS>(a, packed, G, s);
+        default: return launch_mt<8, KS>(a, packed, G, s);
+    }
+}
+
+hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
+                        const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
+                        bool prio, int* S) {
     const WgPlan p = wg_plan(M, N, K);
     WgArgs a;
     a.x = (const uint16_t*)x;
-    a.w0 = (const uint16_t*)w0;
-    a.w1 = (const uint16_t*)(w1 ? w1 : w0);
+    a.w[0] = (const uint16_t*)w0;
+    a.w[1] = (const uint16_t*)(w1 ? w1 : w0);
+    a.w[2] = (const uint16_t*)(w2 ? w2 : a.w[1]);
     a.part = parts;
     a.M = M;
     a.K = K;
     a.N = N;
     a.N0 = N0;
+    a.N1 = N1;
     a.S = p.S;
     a.NX = p.NX;
     a.MCH = p.MCH;
     a.prio = prio ? 1 : 0;
     *S = p.S;
     const int G = p.NX * p.S * p.MCH;
-    switch (p.MT32) {
-        case 1: return launch_mt<1>(a, packed, G, s);
-        case 2: return launch_mt<2>(a, packed, G, s);
-        case 3: return launch_mt<3>(a, packed, G, s);
-        case 4: return launch_mt<4>(a, packed, G, s);
-        case 5: return launch_mt<5>(a, packed, G, s);
-        case 6: return launch_mt<6>(a, packed, G, s);
-        case 7: return launch_mt<7>(a, packed, G, s);
-        default: return launch_mt<8>(a, packed, G, s);
-    }
+    return launch_ks<64>(a, p.MT32, packed, G, s);
 }
 
 // ---- split reduce + epilogue -----------------------------------------------------------
-// Columns [0, N0) -> out0 as FP32 (the router logits of the front GEMM), columns [N0, N)
-// -> out1 (row stride N - N0) with MODE 0 FP32, 1 BF16 (one rounding), 2 BF16 of
-// FP32(add1) + sum.  Four columns per thread; the S partials are added in split order.
+// Of the partial rows (stride N), columns [0, N0) -> out0 as FP32 (the router logits of
+// the front GEMM), columns [N0, N1) -> out1 (row stride N1 - N0) with MODE 0 FP32, 1 BF16
+// (one rounding), 2 BF16 of FP32(add1) + sum; columns from N1 on are left to another
+// consumer.  Four columns per thread; the S partials are added in split order.
 template <int MODE>
 __device__ __forceinline__ void store4(void* out, const void* add, size_t idx, v4f v) {
     if (MODE == 0) {
@@ -296,12 +320,12 @@ __device__ __forceinline__ void store4(void* out, const void* add, size_t idx, v
 }
 
 template <int MODE1>
-__global__ __launch_bounds__(256) void k_wg_reduce(int M, int N, int N0, int S,
+__global__ __launch_bounds__(256) void k_wg_reduce(int M, int N, int N0, int N1, int S,
                                                    const float* __restrict__ part, float* out0,
                                                    void* out1, const void* add1, int prio) {
     if (prio) wave_priority_high();
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    const int n4 = N / 4;
+    const int n4 = N1 / 4;
     if (idx >= (long)M * n4) return;
     const int m = (int)(idx / n4), c = (int)(idx - (long)m * n4) * 4;
     const size_t zs = (size_t)M * N;
@@ -311,20 +335,20 @@ __global__ __launch_bounds__(256) void k_wg_reduce(int M, int N, int N0, int S,
     if (c < N0)
         store4<0>(out0, nullptr, (size_t)m * N0 + c, v);
     else
-        store4<MODE1>(out1, add1, (size_t)m * (N - N0) + (c - N0), v);
+        store4<MODE1>(out1, add1, (size_t)m * (N1 - N0) + (c - N0), v);
 }
 
-hipError_t launch_wg_reduce(int M, int N, int N0, int S, const float* parts, float* out0,
+hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* parts, float* out0,
                             int mode1, void* out1, const void* add1, hipStream_t s, bool prio) {
-    const long n = (long)M * (N / 4);
+    const long n = (long)M * (N1 / 4);
     const dim3 grid((unsigned)((n + 255) / 256)), blk(256);
     const int pr = prio ? 1 : 0;
     if (mode1 == 0)
-        hipLaunchKernelGGL(k_wg_reduce<0>, grid, blk, 0, s, M, N, N0, S, parts, out0, out1, add1, pr);
+        hipLaunchKernelGGL(k_wg_reduce<0>, grid, blk, 0, s, M, N, N0, N1, S, parts, out0, out1, add1, pr);
     else if (mode1 == 1)
-        hipLaunchKernelGGL(k_wg_reduce<1>, grid, blk, 0, s, M, N, N0, S, parts, out0, out1, add1, pr);
+        hipLaunchKernelGGL(k_wg_reduce<1>, grid, blk, 0, s, M, N, N0, N1, S, parts, out0, out1, add1, pr);
     else
-        hipLaunchKernelGGL(k_wg_reduce<2>, grid, blk, 0, s, M, N, N0, S, parts, out0, out1, add1, pr);
+        hipLaunchKernelGGL(k_wg_reduce<2>, grid, blk, 0, s, M, N, N0, N1, S, parts, out0, out1, add1, pr);
     return hipGetLastError();
 }
 

@@ -224,7 +224,7 @@ def main():
     if a.sweep:
         sweep = {}
         for t in (65, 130, 255, 510, 1020):
-            m, Dt, nut, _, _ = run_T(t, max(5, a.steps // 2), 3)
+            m, Dt, nut, _, _ = run_T(t, max(5, a.steps // 2), 50)
             bt = DENSE_BYTES + Dt * EXPERT_BYTES
             sweep[str(t)] = {"us": m * 1e3, "tokens_per_s": t / (m * 1e-3), "D": Dt, "units": nut,
                              "gbs": bt / (m * 1e-3) / 1e9,

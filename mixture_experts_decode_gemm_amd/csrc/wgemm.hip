@@ -193,12 +193,14 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
 // Split count from a cost model: the time is the larger of the MFMA time of the busiest
 // CU (rounds of workgroups) and the HBM time of the weights plus the split partials
 // (written, then read back by the reduce).  Rates are measured ones of this kernel on
-// MI355X: ~5 TFLOP/s per CU in its MFMA loop, ~5.5 TB/s of HBM traffic.
+// MI355X: ~5 TFLOP/s per CU in its MFMA loop, ~5.5 TB/s of HBM traffic.  `share` is the
+// fraction of the GPU the GEMM is planned for (below 1 for a GEMM that runs beside
+// other work: fewer splits, fewer partial bytes).
 struct WgPlan {
     int S, NX, MCH, MT32, KS;
 };
 
-static WgPlan wg_plan(int M, int N, int K) {
+static WgPlan wg_plan(int M, int N, int K, double share) {
     WgPlan p;
     p.NX = (N + 255) / 256;
     p.MCH = (M + 255) / 256;
@@ -206,7 +208,7 @@ static WgPlan wg_plan(int M, int N, int K) {
     p.MT32 = (mt + 31) / 32;
     p.KS = 64;  // (128-deep stages measured no faster at the layer's shapes)
     const int Q = K / (2 * p.KS);
-    const double cus = gemm_device_cus(), rate = 5.0e12, bw = 5.5e12;
+    const double cus = gemm_device_cus() * share, rate = 5.0e12, bw = 5.5e12 * share;
     const double wbytes = (double)N * K * 2 * p.MCH;
     // the token count rounded up to its class (32-token steps, 256-token steps past 256):
     // the plan is the same for every M of a class, so the class end bounds the partials
@@ -235,15 +237,15 @@ bool wgemm_fits(int M, int N, int N0, int N1, int K, bool packed) {
     return N0 % q == 0 && (N1 - N0) % q == 0 && (N - N1) % q == 0;
 }
 
-int wgemm_splits(int M, int N, int K) { return wg_plan(M, N, K).S; }
+int wgemm_splits(int M, int N, int K, double share) { return wg_plan(M, N, K, share).S; }
 
-size_t wgemm_parts_bytes(int M, int N, int K) {
+size_t wgemm_parts_bytes(int M, int N, int K, double share) {
     // the plan depends on M through the 32-token tile count and the 256-token chunks:
     // the largest M of each class bounds its partial buffer
     size_t best = 0;
     for (int m = 32;; m += (m < 256 ? 32 : 256)) {
         const int mm = m < M ? m : M;
-        const size_t b = (size_t)wg_plan(mm, N, K).S * mm * N * sizeof(float);
+        const size_t b = (size_t)wg_plan(mm, N, K, share).S * mm * N * sizeof(float);
         if (b > best) best = b;
         if (m >= M) break;
     }
@@ -275,8 +277,8 @@ static hipError_t launch_ks(const WgArgs& a, int mt32, bool packed, int G, hipSt
 
 hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
                         const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
-                        bool prio, int* S) {
-    const WgPlan p = wg_plan(M, N, K);
+                        bool prio, int* S, double share) {
+    const WgPlan p = wg_plan(M, N, K, share);
     WgArgs a;
     a.x = (const uint16_t*)x;
     a.w[0] = (const uint16_t*)w0;

@@ -481,8 +481,13 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_ffn_bf16(T, K, E, L, I, d->unit_tokens, w->experts.w13, w->experts.w2,
                                 latent, pairs, units, nu, rows, s));
     }
-    MOE_TRY(launch_finalize(T, K, L, rows, wts, nullptr, routed, s));
-    MOE_TRY(launch_rmsnorm(T, L, routed, w->norm_w, d->rms_eps, normed, s));
+    if (finalize_rmsnorm_fits(L)) {
+        MOE_TRY(launch_finalize_rmsnorm(T, K, L, rows, wts, w->norm_w, d->rms_eps, routed, normed,
+                                        s));
+    } else {
+        MOE_TRY(launch_finalize(T, K, L, rows, wts, nullptr, routed, s));
+        MOE_TRY(launch_rmsnorm(T, L, routed, w->norm_w, d->rms_eps, normed, s));
+    }
     // the up-projection added into the shared partial (one rounding)
     if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
     if (fast) {

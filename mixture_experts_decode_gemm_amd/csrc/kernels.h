@@ -82,6 +82,12 @@ hipError_t launch_pack_dense(int N, int K, const void* w, void* out, hipStream_t
 
 hipError_t launch_rmsnorm(int rows, int cols, const void* r, const void* g, float eps, void* out,
                           hipStream_t s);
+// Finalize (no invalid slots) and RMSNorm of each token in one workgroup: routed and normed
+// [T, cols] BF16; cols % 8 == 0 and cols / 8 <= 1024 (finalize_rmsnorm_fits)
+bool finalize_rmsnorm_fits(int cols);
+hipError_t launch_finalize_rmsnorm(int T, int K, int cols, const void* rows, const float* w,
+                                   const void* g, float eps, void* routed, void* normed,
+                                   hipStream_t s);
 hipError_t launch_silu_mul(int M, int S, const void* gu, void* out, hipStream_t s);
 
 }  // namespace moe

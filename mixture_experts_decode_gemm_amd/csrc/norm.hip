@@ -45,6 +45,84 @@ __global__ __launch_bounds__(256) void k_rmsnorm(int cols8, const uint4* __restr
     }
 }
 
+// Finalize and RMSNorm of one token in one workgroup (the layer's own path; the two
+// stand-alone kernels stay for moe_finalize and moe_rmsnorm).  Thread c owns columns
+// 8c .. 8c+7: the top-K weighted sum of its row fragments (one FMA per slot in slot order,
+// as in k_finalize) rounded once to BF16 is the routed latent (written out), then the
+// row's FP32 sum of squares of those BF16 values (per-thread partials, xor shuffles in the
+// wavefront, the wavefronts' partials added in order) gives the RMS scaling of the same
+// registers.  blockDim.x = cols8 rounded up to a wavefront (<= 1024).
+__global__ __launch_bounds__(1024) void k_finalize_rmsnorm(int K, int cols8,
+                                                           const uint4* __restrict__ rows,
+                                                           const float* __restrict__ w,
+                                                           const uint4* __restrict__ g,
+                                                           float eps,
+                                                           uint4* __restrict__ routed,
+                                                           uint4* __restrict__ normed) {
+    __shared__ float part[16];
+    const int t = blockIdx.x, c = threadIdx.x;
+    const bool live = c < cols8;
+    uint4 v[16];
+    float wk[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        wk[k] = k < K ? w[t * K + k] : 0.0f;
+        v[k] = (k < K && live) ? rows[(size_t)(t * K + k) * cols8 + c] : make_uint4(0, 0, 0, 0);
+    }
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (k >= K) continue;
+        const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = __builtin_fmaf(wk[k], bf16_lo(q[i]), acc[2 * i]);
+            acc[2 * i + 1] = __builtin_fmaf(wk[k], bf16_hi(q[i]), acc[2 * i + 1]);
+        }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = bf16_lo(o[i]), b = bf16_hi(o[i]);
+        ss = __builtin_fmaf(a, a, ss);
+        ss = __builtin_fmaf(b, b, ss);
+    }
+    if (live) routed[(size_t)t * cols8 + c] = make_uint4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((c & 63) == 0) part[c >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
+    const float inv = 1.0f / sqrtf(tot / (float)(cols8 * 8) + eps);
+    if (!live) return;
+    const uint4 gw = g[c];
+    const uint32_t h[4] = {gw.x, gw.y, gw.z, gw.w};
+    uint32_t n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        n[i] = pack_bf16x2(bf16_lo(o[i]) * inv * bf16_lo(h[i]), bf16_hi(o[i]) * inv * bf16_hi(h[i]));
+    normed[(size_t)t * cols8 + c] = make_uint4(n[0], n[1], n[2], n[3]);
+}
+
+bool finalize_rmsnorm_fits(int cols) { return cols % 8 == 0 && cols / 8 <= 1024; }
+
+hipError_t launch_finalize_rmsnorm(int T, int K, int cols, const void* rows, const float* w,
+                                   const void* g, float eps, void* routed, void* normed,
+                                   hipStream_t s) {
+    const int cols8 = cols / 8;
+    const int threads = (cols8 + 63) / 64 * 64;
+    hipLaunchKernelGGL(k_finalize_rmsnorm, dim3(T), dim3(threads), 0, s, K, cols8,
+                       (const uint4*)rows, w, (const uint4*)g, eps, (uint4*)routed,
+                       (uint4*)normed);
+    return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(int rows, int cols, const void* r, const void* g, float eps, void* out,
                           hipStream_t s) {
     hipLaunchKernelGGL(k_rmsnorm, dim3(rows), dim3(256), 0, s, cols / 8, (const uint4*)r,

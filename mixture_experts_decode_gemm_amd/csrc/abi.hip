@@ -178,7 +178,7 @@ moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
         if (e != hipSuccess) return MOE_ERR_LAUNCH;
     }
     return launch_status(launch_topk(d->tokens, d->experts, d->top_k, logits, bias,
-                                     d->renormalize, d->routed_scale, ids, weights, s));
+                                     d->renormalize, d->routed_scale, ids, weights, nullptr, s));
 }
 
 size_t moe_lists_workspace_size(const moe_dims* d) {
@@ -199,7 +199,7 @@ moe_status moe_build_lists(const moe_dims* d, const int32_t* ids, int32_t* count
     if (ws_bytes < lists_scratch_bytes(d->tokens, d->experts)) return MOE_ERR_WORKSPACE;
     return launch_status(launch_lists(d->tokens, d->top_k, d->experts, d->unit_tokens, ids, counts,
                                       offsets, pairs, (int32_t*)units, num_units, workspace,
-                                      (hipStream_t)stream));
+                                      nullptr, (hipStream_t)stream));
 }
 
 moe_status moe_quant_mxfp8(int32_t rows, int32_t cols, const void* x, uint8_t* codes,
@@ -468,8 +468,11 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s, 0, true));
     }
     // sigmoid top-K, lists and unit windows
-    MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts, s));
-    MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, s));
+    uint8_t* slot_of = lists_slot_map(uni, T, E);
+    MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts,
+                        slot_of, s));
+    MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, slot_of,
+                         s));
     // MXFP8 latent, grouped experts, Finalize
     if (mx) {
         MOE_TRY(launch_quant_mxfp8(T, L, latent, codes, scales, s));

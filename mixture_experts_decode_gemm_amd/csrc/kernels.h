@@ -14,14 +14,17 @@ hipError_t launch_finalize(int T, int K, int cols, const void* rows, const float
 hipError_t launch_quant_mxfp8(int rows, int cols, const void* x, uint8_t* codes, uint8_t* scales,
                               hipStream_t s);
 
+// slot_of (optional, [T][E] bytes): the slot that chose each chosen expert, for the lists
 hipError_t launch_topk(int T, int E, int K, const float* logits, const float* bias, int renorm,
-                       float scale, int32_t* ids, float* w, hipStream_t s);
+                       float scale, int32_t* ids, float* w, uint8_t* slot_of, hipStream_t s);
 
-// routing lists: scratch of lists_scratch_bytes(T, E) bytes
+// routing lists: scratch of lists_scratch_bytes(T, E) bytes, which ends with the slot map
+// (lists_slot_map) that launch_topk fills; slot_of null: the fill finds the slots in ids
 size_t lists_scratch_bytes(int T, int E);
+uint8_t* lists_slot_map(void* scratch, int T, int E);
 hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32_t* counts,
                         int32_t* offsets, int32_t* pairs, int32_t* units, int32_t* num_units,
-                        void* scratch, hipStream_t s);
+                        void* scratch, const uint8_t* slot_of, hipStream_t s);
 
 // grouped FFN: MXFP4 x MXFP8; the MXFP8 hidden goes to hid [T*K, I] and hid_scales
 // [T*K, I/32] (by pair id); ffn_scratch_bytes(P, I) covers both, 256-aligned.

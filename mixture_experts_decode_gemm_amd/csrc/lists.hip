@@ -11,16 +11,23 @@
 //            exclusive prefix sums over experts (offsets, window indices), the units
 //            (the first window of every touched expert first, then the later windows);
 //   fill  -- one thread per (word, expert): the set bits in ascending token order give
-//            the list entries; the slot k is the first slot of that token holding e.
+//            the list entries; the slot k is the one the top-K recorded in the slot map
+//            (the layer's path), else the first slot of that token holding e.
 // Lists therefore hold ascending pair ids.
 #include "device.h"
 #include "kernels.h"
 
 namespace moe {
 
+// scratch: bitmaps [W][E] and word offsets [W][E] (u32), then the slot map [T][E] (u8)
 size_t lists_scratch_bytes(int T, int E) {
     const size_t W = (size_t)(T + 31) / 32;
-    return 2 * W * (size_t)E * sizeof(uint32_t);
+    return 2 * W * (size_t)E * sizeof(uint32_t) + ((size_t)T * E + 255) / 256 * 256;
+}
+
+uint8_t* lists_slot_map(void* scratch, int T, int E) {
+    const size_t W = (size_t)(T + 31) / 32;
+    return (uint8_t*)scratch + 2 * W * (size_t)E * sizeof(uint32_t);
 }
 
 __global__ __launch_bounds__(256) void k_lists_mark(int T, int K, int E,
@@ -114,6 +121,7 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
                                                     const int32_t* __restrict__ ids,
                                                     const uint32_t* __restrict__ bm,
                                                     const int32_t* __restrict__ wordoff,
+                                                    const uint8_t* __restrict__ slot_of,
                                                     int32_t* __restrict__ pairs) {
     wave_priority_high();
     const int W = (T + 31) / 32;
@@ -126,6 +134,10 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
         const int j = __ffs((int)word) - 1;
         word &= word - 1;
         const int t = w * 32 + j;
+        if (slot_of) {  // the slot the top-K recorded for (t, e)
+            pairs[pos++] = t * K + slot_of[(size_t)t * E + e];
+            continue;
+        }
         // the token's ids are loaded together (no chain of dependent loads); the first
         // slot holding e is the one the bit stands for
         const int32_t* row = ids + (size_t)t * K;
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
 
 hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32_t* counts,
                         int32_t* offsets, int32_t* pairs, int32_t* units, int32_t* num_units,
-                        void* scratch, hipStream_t s) {
+                        void* scratch, const uint8_t* slot_of, hipStream_t s) {
     const int W = (T + 31) / 32;
     uint32_t* bm = (uint32_t*)scratch;
     int32_t* wordoff = (int32_t*)(bm + (size_t)W * E);
@@ -149,7 +161,7 @@ hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32
     hipLaunchKernelGGL(k_lists_scan, dim3(1), dim3(1024), 0, s, T, K, E, unit, bm, wordoff,
                        counts, offsets, (int4*)units, num_units);
     hipLaunchKernelGGL(k_lists_fill, dim3((W * E + 255) / 256), dim3(256), 0, s, T, K, E, ids, bm,
-                       wordoff, pairs);
+                       wordoff, slot_of, pairs);
     return hipGetLastError();
 }
 

@@ -75,10 +75,13 @@ __device__ __forceinline__ void wave_max64(uint32_t& h, uint32_t& l) {
 #undef MOE_DPP
 
 // One wavefront per token.
+// slot_of (optional, [T][E] bytes): slot_of[t][e] = the slot that chose expert e, for
+// the list build (entries of experts a token did not choose are left as they are).
 __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* __restrict__ src,
                                               const float* __restrict__ bias, int renorm,
                                               float scale, int32_t* __restrict__ ids,
-                                              float* __restrict__ weights) {
+                                              float* __restrict__ weights,
+                                              uint8_t* __restrict__ slot_of) {
     wave_priority_high();
     constexpr int PER = 16;
     const int lane = threadIdx.x & 63;
@@ -134,13 +137,14 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
         w = __fmul_rn(w, scale);
         ids[(size_t)t * K + lane] = my_id;
         weights[(size_t)t * K + lane] = w;
+        if (slot_of) slot_of[(size_t)t * E + my_id] = (uint8_t)lane;
     }
 }
 
 hipError_t launch_topk(int T, int E, int K, const float* logits, const float* bias, int renorm,
-                       float scale, int32_t* ids, float* w, hipStream_t s) {
+                       float scale, int32_t* ids, float* w, uint8_t* slot_of, hipStream_t s) {
     hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, T, E, K, logits, bias, renorm,
-                       scale, ids, w);
+                       scale, ids, w, slot_of);
     return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 // E <= 1024) and builds 64-bit selection keys (order-preserving bits of the FP32 key
 // s + bias, then the complemented expert id so that equal keys prefer the lower id).
 // K rounds of a wave-wide maximum (DPP, then readlane) pick the winners in descending
-// order; the winner's lane clears its key.  Lane k keeps slot k's score; the slot-order
+// order; the winner's lane clears its key (found by its unique low word).  Lane k keeps slot k's score; the slot-order
 // FP32 sum, the divide and the routed scale follow.
 //
 // The sigmoid is 1/(1 + E(-x)) with E a defined exponential (Cody-Waite reduction with a
@@ -36,12 +36,13 @@ __device__ __forceinline__ float exp_defined(float z) {
     return ldexpf(p, (int)nf);
 }
 
+// (branch-free: the in-range value is computed for every input and the two clamps are
+// selects, so a wavefront never splits here)
 __device__ __forceinline__ float sigmoid_defined(float logit) {
     const float z = -logit;
-    if (z > 88.0f) return 0.0f;
-    if (z < -87.0f) return 1.0f;
-    const float den = __fadd_rn(1.0f, exp_defined(z));
-    return 1.0f / den;  // IEEE division (correctly rounded by default on gfx950)
+    const float den = __fadd_rn(1.0f, exp_defined(fminf(fmaxf(z, -87.0f), 88.0f)));
+    const float s = 1.0f / den;  // IEEE division (correctly rounded by default on gfx950)
+    return z > 88.0f ? 0.0f : (z < -87.0f ? 1.0f : s);
 }
 
 __device__ __forceinline__ uint32_t order_bits(float f) {
@@ -50,29 +51,29 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide maximum of 64-bit keys (hi, lo), returned in every lane: DPP row shifts by
-// 1, 2, 4, 8 leave each row's maximum in its lane 15, row broadcasts 15 and 31 carry them
-// to lane 63, and a readlane makes it uniform.  Lanes outside a shift's reach combine
-// with 0, the identity (every live key is nonzero).
-__device__ __forceinline__ void dpp_step(uint32_t& h, uint32_t& l, uint32_t oh, uint32_t ol) {
-    const bool gt = oh > h || (oh == h && ol > l);
-    h = gt ? oh : h;
-    l = gt ? ol : l;
+// Wave-wide maximum of 64-bit keys, returned in every lane: DPP row shifts by 1, 2, 4, 8
+// leave each row's maximum in its lane 15, row broadcasts 15 and 31 carry them to lane 63,
+// and a readlane makes it uniform.  Lanes outside a shift's reach combine with 0, the
+// identity (every live key is nonzero).  The keys are compared as 64-bit integers (one
+// 64-bit compare and two selects a step, no scalar mask arithmetic).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ void dpp_max64(uint64_t& k) {
+    const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(k >> 32), CTRL, RMASK, 0xf, false);
+    const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, RMASK, 0xf, false);
+    const uint64_t o = ((uint64_t)h << 32) | l;
+    k = o > k ? o : k;
 }
-#define MOE_DPP(ctrl, rmask)                                                                   \
-    dpp_step(h, l, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, ctrl, rmask, 0xf, false), \
-             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l, ctrl, rmask, 0xf, false))
-__device__ __forceinline__ void wave_max64(uint32_t& h, uint32_t& l) {
-    MOE_DPP(0x111, 0xf);  // row_shr:1
-    MOE_DPP(0x112, 0xf);  // row_shr:2
-    MOE_DPP(0x114, 0xf);  // row_shr:4
-    MOE_DPP(0x118, 0xf);  // row_shr:8
-    MOE_DPP(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
-    MOE_DPP(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
-    h = (uint32_t)__builtin_amdgcn_readlane((int)h, 63);
-    l = (uint32_t)__builtin_amdgcn_readlane((int)l, 63);
+__device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
+    dpp_max64<0x111, 0xf>(k);  // row_shr:1
+    dpp_max64<0x112, 0xf>(k);  // row_shr:2
+    dpp_max64<0x114, 0xf>(k);  // row_shr:4
+    dpp_max64<0x118, 0xf>(k);  // row_shr:8
+    dpp_max64<0x142, 0xa>(k);  // row_bcast:15 into rows 1 and 3
+    dpp_max64<0x143, 0xc>(k);  // row_bcast:31 into rows 2 and 3
+    const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)(k >> 32), 63);
+    const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+    return ((uint64_t)h << 32) | l;
 }
-#undef MOE_DPP
 
 // One wavefront per token.
 // slot_of (optional, [T][E] bytes): slot_of[t][e] = the slot that chose expert e, for
@@ -87,41 +88,44 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // uniform per wavefront
-    uint32_t khi[PER], klo[PER];
+    uint64_t key[PER];  // (order bits of s + bias) << 32 | ~e; 0 where the lane has no expert
     float sc[PER];
+    // every logit and bias of this lane is loaded before the first use (clamped indices,
+    // no branches), so the wavefront waits for one round trip, not one per expert
+    float lg[PER], bi[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int e = min(j * 64 + lane, E - 1);
+        lg[j] = src[(size_t)t * E + e];
+        bi[j] = bias[e];
+    }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = j * 64 + lane;
-        if (e < E) {
-            const float s = sigmoid_defined(src[(size_t)t * E + e]);
-            sc[j] = s;
-            khi[j] = order_bits(__fadd_rn(s, bias[e]));
-            klo[j] = ~(uint32_t)e;
-        } else {
-            sc[j] = 0.0f;
-            khi[j] = 0;
-            klo[j] = 0;
-        }
+        const float s = sigmoid_defined(lg[j]);
+        const bool live = e < E;
+        sc[j] = live ? s : 0.0f;
+        key[j] = live ? ((uint64_t)order_bits(__fadd_rn(s, bi[j])) << 32) | (uint32_t)~(uint32_t)e
+                      : 0ull;
     }
     float mine = 0.0f;  // lane k holds the score chosen for slot k
     int my_id = 0;
     for (int k = 0; k < K; ++k) {
-        uint32_t bh = 0, bl = 0;
+        uint64_t best = 0;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) dpp_step(bh, bl, khi[j], klo[j]);
-        wave_max64(bh, bl);
-        const int win = (int)(~bl);  // uniform
-        const int owner = win & 63, jw = win >> 6;
+        for (int j = 0; j < PER; ++j) best = key[j] > best ? key[j] : best;
+        best = wave_max64(best);
+        const uint32_t wl = (uint32_t)best;  // ~winner id: unique in the wavefront
+        const int win = (int)(~wl);          // uniform
+        const int owner = win & 63;
+        // the owner lane drops the winning key and takes its score (matched by the unique
+        // low word; no other lane matches)
         float sel = 0.0f;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            if (j == jw) {
-                sel = sc[j];
-                if (lane == owner) {
-                    khi[j] = 0;
-                    klo[j] = 0;
-                }
-            }
+            const bool hit = (uint32_t)key[j] == wl;
+            sel = hit ? sc[j] : sel;
+            key[j] = hit ? 0ull : key[j];
         }
         const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel), owner));
         if (lane == k) {

@@ -449,8 +449,14 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         // x; FP32 logits and the latent rounded once to BF16 from the same partials
         MOE_TRY(launch_wgemm(T, E + L, E, E + L, H, x, w->w_gate, w->w_down, nullptr, dpack, parts,
                              s, true, &s_fr));
-        MOE_TRY(launch_wg_reduce(T, E + L, E, E + L, s_fr, parts, logits, 1, latent, nullptr, s,
-                                 true));
+        // FP32 logits; the latent rounded once to BF16 and, for MXFP4 experts, its MXFP8
+        // codes in the same pass
+        if (mx)
+            MOE_TRY(launch_wg_reduce_front(T, E + L, E, E + L, s_fr, parts, logits, latent, codes,
+                                           scales, s));
+        else
+            MOE_TRY(launch_wg_reduce(T, E + L, E, E + L, s_fr, parts, logits, 1, latent, nullptr,
+                                     s, true));
     } else {
         // The shared expert depends on x only: it runs on the side stream beside the whole
         // routed path; gate/up as split-K partials, whose sum the activation rounds (the
@@ -475,7 +481,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
                          s));
     // MXFP8 latent, grouped experts, Finalize
     if (mx) {
-        MOE_TRY(launch_quant_mxfp8(T, L, latent, codes, scales, s));
+        if (!fast) MOE_TRY(launch_quant_mxfp8(T, L, latent, codes, scales, s));
         MOE_TRY(launch_ffn_mx(T, K, E, L, I, d->unit_tokens, (const uint8_t*)w->experts.w13,
                               (const uint8_t*)w->experts.s13, (const uint8_t*)w->experts.w2,
                               (const uint8_t*)w->experts.s2, codes, scales, pairs, units, nu,

@@ -64,6 +64,29 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
     return sign | code;
 }
 
+// One MXFP8 block of 32 BF16 values given as 16 words of BF16 pairs (element 2i in the low
+// half of word i): the E8M0 exponent X (returned) from the block's largest magnitude and
+// the 32 E4M3 codes of v / 2^X, four to a word in element order.
+__device__ __forceinline__ int mxfp8_encode_block(const uint32_t (&q)[16], uint32_t (&out)[8]) {
+    uint32_t amax = 0;  // magnitude bits order like magnitudes for finite BF16
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t lo = q[i] & 0x7FFFu, hi = (q[i] >> 16) & 0x7FFFu;
+        amax = amax > lo ? amax : lo;
+        amax = amax > hi ? amax : hi;
+    }
+    const int X = mx_block_exponent(amax << 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t c0 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i]), -X));
+        const uint32_t c1 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i]), -X));
+        const uint32_t c2 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i + 1]), -X));
+        const uint32_t c3 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i + 1]), -X));
+        out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    return X;
+}
+
 // ---- workgroup barrier over LDS only ----------------------------------------------------
 // __syncthreads() fences global memory too, which makes every wavefront wait for all of
 // its outstanding global loads (s_waitcnt vmcnt(0)) -- fatal to a software pipeline that

@@ -23,23 +23,8 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(long nblocks, const uint4* 
         q[4 * i + 2] = v.z;
         q[4 * i + 3] = v.w;
     }
-    uint32_t amax = 0;  // magnitude bits order like magnitudes for finite BF16
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        uint32_t lo = q[i] & 0x7FFFu, hi = (q[i] >> 16) & 0x7FFFu;
-        amax = amax > lo ? amax : lo;
-        amax = amax > hi ? amax : hi;
-    }
-    const int X = mx_block_exponent(amax << 16);
     uint32_t out[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t c0 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i]), -X));
-        uint32_t c1 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i]), -X));
-        uint32_t c2 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i + 1]), -X));
-        uint32_t c3 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i + 1]), -X));
-        out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    }
+    const int X = mxfp8_encode_block(q, out);
     codes[b * 2] = make_uint4(out[0], out[1], out[2], out[3]);
     codes[b * 2 + 1] = make_uint4(out[4], out[5], out[6], out[7]);
     scales[b] = (uint8_t)(X + 127);

@@ -354,6 +354,65 @@ hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* pa
     return hipGetLastError();
 }
 
+// The front GEMM's reduce with the MXFP8 quantisation of the latent folded in: threads
+// below M * N0/4 add four logit columns each (FP32 out); each later thread owns one
+// 32-column block of one token's latent, adds its split partials in split order, rounds
+// them once to BF16 (the latent, written out) and writes the block's E4M3 codes and E8M0
+// scale.
+__global__ __launch_bounds__(256) void k_wg_reduce_front(int M, int N, int N0, int N1, int S,
+                                                         const float* __restrict__ part,
+                                                         float* __restrict__ logits,
+                                                         uint4* __restrict__ latent,
+                                                         uint4* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+    wave_priority_high();
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const size_t zs = (size_t)M * N;
+    const long nlog = (long)M * (N0 / 4);
+    if (idx < nlog) {
+        const int m = (int)(idx / (N0 / 4)), c = (int)(idx - (long)m * (N0 / 4)) * 4;
+        const float* p = part + (size_t)m * N + c;
+        v4f v = *(const v4f*)p;
+        for (int zz = 1; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
+        *(v4f*)(logits + (size_t)m * N0 + c) = v;
+        return;
+    }
+    const int cbs = (N1 - N0) / 32;
+    const long b = idx - nlog;
+    if (b >= (long)M * cbs) return;
+    const int m = (int)(b / cbs), cb = (int)(b - (long)m * cbs);
+    const float* p = part + (size_t)m * N + N0 + cb * 32;
+    v4f v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *(const v4f*)(p + 4 * i);
+    for (int zz = 1; zz < S; ++zz)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += *(const v4f*)(p + zz * zs + 4 * i);
+    uint32_t q[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        q[2 * i] = pack_bf16x2(v[i][0], v[i][1]);
+        q[2 * i + 1] = pack_bf16x2(v[i][2], v[i][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        latent[b * 4 + i] = make_uint4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+    uint32_t out[8];
+    const int X = mxfp8_encode_block(q, out);
+    codes[b * 2] = make_uint4(out[0], out[1], out[2], out[3]);
+    codes[b * 2 + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+    scales[b] = (uint8_t)(X + 127);
+}
+
+hipError_t launch_wg_reduce_front(int M, int N, int N0, int N1, int S, const float* parts,
+                                  float* logits, void* latent, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t s) {
+    const long n = (long)M * (N0 / 4) + (long)M * ((N1 - N0) / 32);
+    hipLaunchKernelGGL(k_wg_reduce_front, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M, N,
+                       N0, N1, S, parts, logits, (uint4*)latent, (uint4*)codes, scales);
+    return hipGetLastError();
+}
+
 // ---- packed dense layout ---------------------------------------------------------------
 // W [N, K] BF16 row-major -> blocks of 1 KiB: [N/64 row groups][K/64 K stages][tile 2]
 // [K step 4][lane 64][8 BF16], lane l of (group g, stage s, tile i, step q) holding row

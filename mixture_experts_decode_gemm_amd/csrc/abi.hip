@@ -17,9 +17,11 @@ constexpr int kMaxTokens = 4096;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 // the GPU share the shared expert's GEMMs are planned for: they run beside the routing
-// kernels and the expert passes, so fewer, longer splits (half the partial bytes) serve
-// better than filling every CU (measured: 0.5 best of 0.3 .. 1; 547 -> 521 us per layer)
-constexpr double kSideShare = 0.5;
+// kernels (gate/up) and the expert passes (down), so fewer, longer splits (fewer partial
+// bytes) serve better than filling every CU (measured for both at once: 0.5 best of
+// 0.3 .. 1; 547 -> 521 us per layer)
+constexpr double kSideShareGu = 0.5;
+constexpr double kSideShareDown = 0.5;
 
 inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t up256(size_t b) { return (b + 255) / 256 * 256; }
@@ -91,8 +93,8 @@ Layout layout(const moe_dims* d) {
     lo.uni_side = at;
     size_t us = 0;
     const size_t g2[4] = {gemm_parts_bytes(Tm, S2, Hi), gemm_scratch_bytes(Tm, Hi, d->shared_inter),
-                          wgemm_parts_bytes(Tm, S2, Hi, kSideShare),
-                          wgemm_parts_bytes(Tm, Hi, d->shared_inter, kSideShare)};
+                          wgemm_parts_bytes(Tm, S2, Hi, kSideShareGu),
+                          wgemm_parts_bytes(Tm, Hi, d->shared_inter, kSideShareDown)};
     for (size_t v : g2) us = v > us ? v : us;
     at += up256(us);
     lo.parts = at;
@@ -438,12 +440,12 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
             MOE_TRY(hipStreamWaitEvent(sh, ss->fork, 0));
         }
         MOE_TRY(launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_gu, kSideShare));
+                             parts_side, sh, false, &s_gu, kSideShareGu));
         MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh));
+        // the down GEMM's split partials stay in the side scratch: the up-projection's
+        // reduce adds them (shared rounded once to BF16) before it adds its own
         MOE_TRY(launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_sd, kSideShare));
-        MOE_TRY(launch_wg_reduce(T, H, 0, H, s_sd, parts_side, nullptr, 1, shared, nullptr, sh,
-                                 false));
+                             parts_side, sh, false, &s_sd, kSideShareDown));
         if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
         // [wide] front: the router rows and the latent down rows as one FP32-out GEMM over
         // x; FP32 logits and the latent rounded once to BF16 from the same partials
@@ -474,7 +476,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s, 0, true));
     }
     // sigmoid top-K, lists and unit windows
-    uint8_t* slot_of = lists_slot_map(uni, T, E);
+    uint8_t* slot_of = lists_fused_fits(T, E) ? nullptr : lists_slot_map(uni, T, E);
     MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts,
                         slot_of, s));
     MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, slot_of,
@@ -497,13 +499,15 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_finalize(T, K, L, rows, wts, nullptr, routed, s));
         MOE_TRY(launch_rmsnorm(T, L, routed, w->norm_w, d->rms_eps, normed, s));
     }
-    // the up-projection added into the shared partial (one rounding)
-    if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
+    // the up-projection added into the shared partial (one rounding); only its reduce
+    // needs the side stream's results
     if (fast) {
         MOE_TRY(launch_wgemm(T, H, H, H, L, normed, w->w_up, nullptr, nullptr, dpack, parts, s,
                              false, &s_up));
-        MOE_TRY(launch_wg_reduce(T, H, 0, H, s_up, parts, nullptr, 2, out, shared, s, false));
+        if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
+        MOE_TRY(launch_wg_reduce_combine(T, H, s_up, parts, s_sd, parts_side, shared, out, s));
     } else {
+        if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
         MOE_TRY(launch_gemm(T, H, L, normed, w->w_up, out, shared, 2, uni, s));
     }
 #undef MOE_TRY

@@ -13,7 +13,8 @@
 //   fill  -- one thread per (word, expert): the set bits in ascending token order give
 //            the list entries; the slot k is the one the top-K recorded in the slot map
 //            (the layer's path), else the first slot of that token holding e.
-// Lists therefore hold ascending pair ids.
+// Lists therefore hold ascending pair ids.  Batches whose bitmaps fit in LDS take one
+// launch instead (k_lists_fused).
 #include "device.h"
 #include "kernels.h"
 
@@ -151,9 +152,96 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
     }
 }
 
+// The whole build in one workgroup when the bitmaps fit in LDS (decode batches up to a
+// few hundred tokens): the three steps above with the bitmaps and list offsets in LDS and
+// block barriers between them, and a scatter fill -- the thread of token t places each of
+// its pairs (t, k) at offsets[e] + (the tokens before t that chose e: set bits of e's
+// bitmap below t).  A slot repeating an earlier slot's id is dropped, as in the marking.
+__global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int unit,
+                                                      const int32_t* __restrict__ ids,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int4* __restrict__ units,
+                                                      int32_t* __restrict__ num_units,
+                                                      int32_t* __restrict__ pairs) {
+    wave_priority_high();
+    extern __shared__ uint32_t lds_lists[];
+    __shared__ int smem[17];
+    const int W = (T + 31) / 32;
+    uint32_t* bm = lds_lists;                // [W][E]
+    int* offl = (int*)(lds_lists + W * E);   // [E]
+    for (int i = threadIdx.x; i < W * E; i += 1024) bm[i] = 0;
+    __syncthreads();
+    for (int q = threadIdx.x; q < T * K; q += 1024) {
+        const int e = ids[q];
+        const int t = q / K;
+        if (e >= 0 && e < E) atomicOr(&bm[(t >> 5) * E + e], 1u << (t & 31));
+    }
+    __syncthreads();
+    const int e = threadIdx.x;
+    int c = 0;
+    if (e < E)
+        for (int w = 0; w < W; ++w) c += __popc(bm[w * E + e]);
+    int total_pairs, touched, later_total;
+    const int off = block_exclusive_scan_1024(c, smem, &total_pairs);
+    const int nu = (c + unit - 1) / unit;
+    const int fi = block_exclusive_scan_1024(c > 0 ? 1 : 0, smem, &touched);
+    const int li = block_exclusive_scan_1024(nu > 1 ? nu - 1 : 0, smem, &later_total);
+    if (e < E) {
+        offl[e] = off;
+        counts[e] = c;
+        offsets[e] = off;
+        if (c > 0) units[fi] = make_int4(e, off, c < unit ? c : unit, c);
+        for (int j = 1; j < nu; ++j) {
+            const int rest = c - j * unit;
+            units[touched + li + j - 1] = make_int4(e, off + j * unit, rest < unit ? rest : unit, 0);
+        }
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = total_pairs;
+        num_units[0] = touched + later_total;
+        num_units[1] = T * K - total_pairs;
+        num_units[2] = touched;
+        num_units[3] = 0;
+    }
+    __syncthreads();  // offl complete
+    for (int t = threadIdx.x; t < T; t += 1024) {
+        const int32_t* row = ids + (size_t)t * K;
+        int32_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = k < K ? row[k] : -1;
+        const int w = t >> 5;
+        const uint32_t below = (1u << (t & 31)) - 1u;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int ek = v[k];
+            bool first = k < K && ek >= 0 && ek < E;
+#pragma unroll
+            for (int k2 = 0; k2 < k; ++k2) first = first && v[k2] != ek;
+            if (!first) continue;
+            int pos = offl[ek] + __popc(bm[w * E + ek] & below);
+            for (int w2 = 0; w2 < w; ++w2) pos += __popc(bm[w2 * E + ek]);
+            pairs[pos] = t * K + k;
+        }
+    }
+}
+
+// LDS bytes of the one-workgroup build (bitmaps + list offsets); it runs when this is at
+// most 60 KiB and E <= 1024
+static size_t lists_fused_lds(int T, int E) {
+    return ((size_t)(T + 31) / 32 * E + E) * sizeof(uint32_t);
+}
+
+bool lists_fused_fits(int T, int E) { return E <= 1024 && lists_fused_lds(T, E) <= 61440; }
+
 hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32_t* counts,
                         int32_t* offsets, int32_t* pairs, int32_t* units, int32_t* num_units,
                         void* scratch, const uint8_t* slot_of, hipStream_t s) {
+    if (lists_fused_fits(T, E)) {
+        hipLaunchKernelGGL(k_lists_fused, dim3(1), dim3(1024), lists_fused_lds(T, E), s, T, K, E,
+                           unit, ids, counts, offsets, (int4*)units, num_units, pairs);
+        return hipGetLastError();
+    }
     const int W = (T + 31) / 32;
     uint32_t* bm = (uint32_t*)scratch;
     int32_t* wordoff = (int32_t*)(bm + (size_t)W * E);

@@ -44,7 +44,7 @@ struct WgArgs {
     const uint16_t* x;     // [M, K] BF16
     const uint16_t* w[3];  // row segments [0, N0), [N0, N1), [N1, N): row-major or packed
     float* part;           // [S][M][N] FP32
-    int M, K, N, N0, N1, S, NX, MCH, prio;
+    int M, K, N, N0, N1, S, NX, MCH, prio;  // M chunks of 32 * MT32 tokens
 };
 
 // MT32: 32-token tiles computed per token chunk (1..8); KS: K depth of one LDS stage (64
@@ -70,14 +70,16 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
     if (a.prio) wave_priority_high();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, h = lane >> 5;
+    // items: token chunk fastest, then weight tile, then K split -- the chunks of one
+    // weight tile are neighbours on one XCD and share its weights through L2
     const int item = wg_xcd_item(blockIdx.x, a.NX * a.S * a.MCH);
-    const int nt = item % a.NX, rest = item / a.NX;
-    const int z = rest % a.S, mc = rest / a.S;
+    const int mc = item % a.MCH, rest = item / a.MCH;
+    const int nt = rest % a.NX, z = rest / a.NX;
     const int Q = a.K / (2 * KS);  // K in pairs of stages
     const int q0 = z * Q / a.S, q1 = (z + 1) * Q / a.S;
     const int kb = q0 * 2 * KS, nst = (q1 - q0) * 2;
     const int n0 = nt * 256 + wave * 32;  // this wavefront's 32 output rows
-    const int m0 = mc * 256;
+    const int m0 = mc * 32 * MT32;
 
     // weight rows of this wavefront (past N: a valid tile, loaded but never stored)
     const int nrow = min(n0, a.N - 32);
@@ -200,34 +202,40 @@ struct WgPlan {
     int S, NX, MCH, MT32, KS;
 };
 
+// Token chunks: 256 tokens (MT32 = 8; fewer for M < 256) or 128 (MT32 = 4, twice the
+// workgroups for the same split count); the chunks of one weight tile read its weights
+// once from HBM (neighbouring items on one XCD).  Token counts fall in classes (32-token
+// steps up to 256, 128-token steps past it) with one plan each.
+static int wg_class(int M) { return M <= 256 ? (M + 31) / 32 * 32 : (M + 127) / 128 * 128; }
+
 static WgPlan wg_plan(int M, int N, int K, double share) {
-    WgPlan p;
-    p.NX = (N + 255) / 256;
-    p.MCH = (M + 255) / 256;
-    const int mt = M < 256 ? M : 256;
-    p.MT32 = (mt + 31) / 32;
-    p.KS = 64;  // (128-deep stages measured no faster at the layer's shapes)
-    const int Q = K / (2 * p.KS);
+    const int KS = 64;  // (128-deep stages measured no faster at the layer's shapes)
+    const int NX = (N + 255) / 256;
+    const int Q = K / (2 * KS);
     const double cus = gemm_device_cus() * share, rate = 5.0e12, bw = 5.5e12 * share;
-    const double wbytes = (double)N * K * 2 * p.MCH;
-    // the token count rounded up to its class (32-token steps, 256-token steps past 256):
-    // the plan is the same for every M of a class, so the class end bounds the partials
-    const double Mc = M <= 256 ? (double)p.MT32 * 32 : (double)p.MCH * 256;
+    const double wbytes = (double)N * K * 2;
+    // the class end bounds the partials: the plan is the same for every M of a class
+    const double Mc = wg_class(M);
+    WgPlan best_p{1, NX, 1, 1, KS};
     double best = 1e30;
-    p.S = 1;
-    for (int S = 1; S <= Q && S <= 64; ++S) {
-        const double wgs = (double)p.NX * p.MCH * S;
-        const double rounds = (double)(long)((wgs + cus - 1) / cus);
-        const double kz = (double)((Q + S - 1) / S) * 2 * p.KS;  // the longest K range
-        const double t_mfma = rounds * 2.0 * 256 * (32.0 * p.MT32) * kz / rate;
-        const double t_hbm = (wbytes + 2.0 * S * Mc * N * 4) / bw;
-        const double t = t_mfma > t_hbm ? t_mfma : t_hbm;
-        if (t < best * 0.995) {
-            best = t;
-            p.S = S;
+    for (int chunk = 256; chunk >= 128; chunk /= 2) {
+        if (chunk == 128 && M <= 128) break;
+        const int mch = (M + chunk - 1) / chunk;
+        const int mt32 = M < chunk ? (M + 31) / 32 : chunk / 32;
+        for (int S = 1; S <= Q && S <= 64; ++S) {
+            const double wgs = (double)NX * mch * S;
+            const double rounds = (double)(long)((wgs + cus - 1) / cus);
+            const double kz = (double)((Q + S - 1) / S) * 2 * KS;  // the longest K range
+            const double t_mfma = rounds * 2.0 * 256 * (32.0 * mt32) * kz / rate;
+            const double t_hbm = (wbytes + 2.0 * S * Mc * N * 4) / bw;
+            const double t = t_mfma > t_hbm ? t_mfma : t_hbm;
+            if (t < best * 0.995) {
+                best = t;
+                best_p = WgPlan{S, NX, mch, mt32, KS};
+            }
         }
     }
-    return p;
+    return best_p;
 }
 
 bool wgemm_fits(int M, int N, int N0, int N1, int K, bool packed) {
@@ -243,7 +251,7 @@ size_t wgemm_parts_bytes(int M, int N, int K, double share) {
     // the plan depends on M through the 32-token tile count and the 256-token chunks:
     // the largest M of each class bounds its partial buffer
     size_t best = 0;
-    for (int m = 32;; m += (m < 256 ? 32 : 256)) {
+    for (int m = 32;; m += (m < 256 ? 32 : 128)) {
         const int mm = m < M ? m : M;
         const size_t b = (size_t)wg_plan(mm, N, K, share).S * mm * N * sizeof(float);
         if (b > best) best = b;
@@ -351,6 +359,41 @@ hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* pa
         hipLaunchKernelGGL(k_wg_reduce<1>, grid, blk, 0, s, M, N, N0, N1, S, parts, out0, out1, add1, pr);
     else
         hipLaunchKernelGGL(k_wg_reduce<2>, grid, blk, 0, s, M, N, N0, N1, S, parts, out0, out1, add1, pr);
+    return hipGetLastError();
+}
+
+// The up-projection's reduce with the shared expert's down-projection reduce folded in:
+// shared = BF16(the S2 shared partials added in split order), written out, then out =
+// BF16(FP32(shared) + the S up partials added in split order) -- the same two roundings
+// as reducing the shared partials on their own first.  Four columns a thread.
+__global__ __launch_bounds__(256) void k_wg_reduce_combine(int M, int N, int S,
+                                                           const float* __restrict__ part, int S2,
+                                                           const float* __restrict__ part2,
+                                                           uint2* __restrict__ shared,
+                                                           uint2* __restrict__ out) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)M * (N / 4)) return;
+    const size_t zs = (size_t)M * N;
+    const float* p2 = part2 + idx * 4;
+    const float* p = part + idx * 4;
+    v4f a = *(const v4f*)p2;
+    v4f v = *(const v4f*)p;
+    for (int zz = 1; zz < S2; ++zz) a += *(const v4f*)(p2 + zz * zs);
+    for (int zz = 1; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
+    const uint2 sh = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    shared[idx] = sh;
+    v[0] += bf16_lo(sh.x);
+    v[1] += bf16_hi(sh.x);
+    v[2] += bf16_lo(sh.y);
+    v[3] += bf16_hi(sh.y);
+    out[idx] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
+hipError_t launch_wg_reduce_combine(int M, int N, int S, const float* parts, int S2,
+                                    const float* parts2, void* shared, void* out, hipStream_t s) {
+    const long n = (long)M * (N / 4);
+    hipLaunchKernelGGL(k_wg_reduce_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M,
+                       N, S, parts, S2, parts2, (uint2*)shared, (uint2*)out);
     return hipGetLastError();
 }
 

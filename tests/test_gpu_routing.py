@@ -104,8 +104,10 @@ def test_topk_saturated_logits(orc):
         assert np.array_equal(ids, rid) and np.array_equal(w.view(np.uint32), rw.view(np.uint32))
 
 
-def test_lists_drop_invalid_and_repeated_ids(orc):
-    T, K, E = 70, 4, 9
+# (70, 4, 9): the one-workgroup build (bitmaps in LDS); (1100, 4, 1024): bitmaps past the
+# LDS bound, the three-launch build
+@pytest.mark.parametrize("T,K,E", [(70, 4, 9), (1100, 4, 1024)])
+def test_lists_drop_invalid_and_repeated_ids(orc, T, K, E):
     g = np.random.default_rng(12)
     ids = g.integers(-2, E + 2, size=(T, K)).astype(np.int32)
     d = moe.dims(T, T, experts=E, top_k=K)
@@ -113,8 +115,9 @@ def test_lists_drop_invalid_and_repeated_ids(orc):
     assert got["dropped"] > 0
 
 
-def test_lists_hot_expert_many_units(orc):
-    T, K, E = 1020, 16, 896
+@pytest.mark.parametrize("T", [256, 1020])  # one-workgroup build, three-launch build
+def test_lists_hot_expert_many_units(orc, T):
+    K, E = 16, 896
     ids = np.zeros((T, K), np.int32)
     for t in range(T):
         ids[t] = np.r_[0, 1 + (np.arange(15) + t) % (E - 1)]

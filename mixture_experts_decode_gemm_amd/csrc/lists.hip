@@ -152,11 +152,71 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
     }
 }
 
+// Exclusive prefix sums of three values at once over a 1024-thread block (one pass:
+// wave scans by shuffles, the 16 wave totals scanned by one wavefront); totals returned.
+__device__ int3 block_exclusive_scan3_1024(int3 v, int3* smem, int3* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int3 x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int a = __shfl_up(x.x, off, 64), b = __shfl_up(x.y, off, 64),
+                  c = __shfl_up(x.z, off, 64);
+        if (lane >= off) {
+            x.x += a;
+            x.y += b;
+            x.z += c;
+        }
+    }
+    if (lane == 63) smem[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int3 w = lane < 16 ? smem[lane] : make_int3(0, 0, 0);
+        int3 y = w;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int a = __shfl_up(y.x, off, 64), b = __shfl_up(y.y, off, 64),
+                      c = __shfl_up(y.z, off, 64);
+            if (lane >= off) {
+                y.x += a;
+                y.y += b;
+                y.z += c;
+            }
+        }
+        if (lane < 16) smem[lane] = make_int3(y.x - w.x, y.y - w.y, y.z - w.z);
+        if (lane == 15) smem[16] = y;
+    }
+    __syncthreads();
+    const int3 base = smem[wave];
+    *total = smem[16];
+    return make_int3(base.x + x.x - v.x, base.y + x.y - v.y, base.z + x.z - v.z);
+}
+
+// the K ids of token t (-1 past K), loaded together
+__device__ __forceinline__ void load_token_ids(const int32_t* __restrict__ ids, int t, int K,
+                                               int32_t v[16]) {
+    const int32_t* row = ids + (size_t)t * K;
+    if (K == 16) {  // 64-byte rows: four 16-byte loads
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int4 q = ((const int4*)row)[i];
+            v[4 * i] = q.x;
+            v[4 * i + 1] = q.y;
+            v[4 * i + 2] = q.z;
+            v[4 * i + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = k < K ? row[k] : -1;
+    }
+}
+
 // The whole build in one workgroup when the bitmaps fit in LDS (decode batches up to a
 // few hundred tokens): the three steps above with the bitmaps and list offsets in LDS and
 // block barriers between them, and a scatter fill -- the thread of token t places each of
 // its pairs (t, k) at offsets[e] + (the tokens before t that chose e: set bits of e's
 // bitmap below t).  A slot repeating an earlier slot's id is dropped, as in the marking.
+// Thread i owns tokens i, i + 1024, ...; the ids of its first token stay in registers
+// between the marking and the fill.
 __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int unit,
                                                       const int32_t* __restrict__ ids,
                                                       int32_t* __restrict__ counts,
@@ -166,27 +226,40 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
                                                       int32_t* __restrict__ pairs) {
     wave_priority_high();
     extern __shared__ uint32_t lds_lists[];
-    __shared__ int smem[17];
+    __shared__ int3 smem[17];
     const int W = (T + 31) / 32;
     uint32_t* bm = lds_lists;                // [W][E]
     int* offl = (int*)(lds_lists + W * E);   // [E]
+    const int t0 = threadIdx.x;
+    int32_t v0[16];
+    if (t0 < T) load_token_ids(ids, t0, K, v0);
     for (int i = threadIdx.x; i < W * E; i += 1024) bm[i] = 0;
     __syncthreads();
-    for (int q = threadIdx.x; q < T * K; q += 1024) {
-        const int e = ids[q];
-        const int t = q / K;
-        if (e >= 0 && e < E) atomicOr(&bm[(t >> 5) * E + e], 1u << (t & 31));
+    auto mark = [&](int t, const int32_t v[16]) {
+        const uint32_t bit = 1u << (t & 31);
+        uint32_t* row = bm + (t >> 5) * E;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (k < K && v[k] >= 0 && v[k] < E) atomicOr(&row[v[k]], bit);
+    };
+    if (t0 < T) mark(t0, v0);
+    for (int t = t0 + 1024; t < T; t += 1024) {
+        int32_t v[16];
+        load_token_ids(ids, t, K, v);
+        mark(t, v);
     }
     __syncthreads();
     const int e = threadIdx.x;
     int c = 0;
     if (e < E)
         for (int w = 0; w < W; ++w) c += __popc(bm[w * E + e]);
-    int total_pairs, touched, later_total;
-    const int off = block_exclusive_scan_1024(c, smem, &total_pairs);
     const int nu = (c + unit - 1) / unit;
-    const int fi = block_exclusive_scan_1024(c > 0 ? 1 : 0, smem, &touched);
-    const int li = block_exclusive_scan_1024(nu > 1 ? nu - 1 : 0, smem, &later_total);
+    // list offsets; the first window of every touched expert first, then every later window
+    int3 tot;
+    const int3 ex = block_exclusive_scan3_1024(make_int3(c, c > 0 ? 1 : 0, nu > 1 ? nu - 1 : 0),
+                                               smem, &tot);
+    const int off = ex.x, fi = ex.y, li = ex.z;
+    const int total_pairs = tot.x, touched = tot.y, later_total = tot.z;
     if (e < E) {
         offl[e] = off;
         counts[e] = c;
@@ -205,11 +278,7 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
         num_units[3] = 0;
     }
     __syncthreads();  // offl complete
-    for (int t = threadIdx.x; t < T; t += 1024) {
-        const int32_t* row = ids + (size_t)t * K;
-        int32_t v[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = k < K ? row[k] : -1;
+    auto fill = [&](int t, const int32_t v[16]) {
         const int w = t >> 5;
         const uint32_t below = (1u << (t & 31)) - 1u;
 #pragma unroll
@@ -223,6 +292,12 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
             for (int w2 = 0; w2 < w; ++w2) pos += __popc(bm[w2 * E + ek]);
             pairs[pos] = t * K + k;
         }
+    };
+    if (t0 < T) fill(t0, v0);
+    for (int t = t0 + 1024; t < T; t += 1024) {
+        int32_t v[16];
+        load_token_ids(ids, t, K, v);
+        fill(t, v);
     }
 }
 

@@ -2,12 +2,13 @@
 // router's sigmoid top-16 over one group with the correction bias, renormalize and
 // scale; wide page, WideRoute: an exact top-16 with renormalised weights).
 //
-// One wavefront per token.  Each lane owns experts lane, lane+64, ... (<= 16 per lane,
-// E <= 1024) and builds 64-bit selection keys (order-preserving bits of the FP32 key
-// s + bias, then the complemented expert id so that equal keys prefer the lower id).
-// K rounds of a wave-wide maximum (DPP, then readlane) pick the winners in descending
-// order; the winner's lane clears its key (found by its unique low word).  Lane k keeps slot k's score; the slot-order
-// FP32 sum, the divide and the routed scale follow.
+// One workgroup of four wavefronts per token.  Each lane owns four experts (E <= 1024)
+// and builds 64-bit selection keys (order-preserving bits of the FP32 key s + bias, then
+// the complemented expert id so that equal keys prefer the lower id).  Rounds of a
+// wave-wide maximum (DPP, then readlane) pick winners in descending order, first within
+// each wavefront, then among the wavefronts' winners; the winner's lane clears its key.
+// Lane k keeps slot k's score; the slot-order FP32 sum, the divide and the routed scale
+// follow.
 //
 // The sigmoid is 1/(1 + E(-x)) with E a defined exponential (Cody-Waite reduction with a
 // 16-significant-bit head of ln 2, degree-7 Taylor polynomial by Horner's rule, scaling
@@ -75,7 +76,11 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
     return ((uint64_t)h << 32) | l;
 }
 
-// One wavefront per token.
+// One 256-thread workgroup per token.  Wavefront w owns experts w*64 + lane + 256 j
+// (j < 4, E <= 1024) and finds its own top-K in K rounds (its K winners, keys and scores,
+// to LDS); wavefront 0 then takes the 4K candidates, one a lane, and picks the token's
+// top-K from them in K more rounds.  Keys are unique, so the winners and their order are
+// those of one top-K over all E keys.
 // slot_of (optional, [T][E] bytes): slot_of[t][e] = the slot that chose expert e, for
 // the list build (entries of experts a token did not choose are left as they are).
 __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* __restrict__ src,
@@ -84,10 +89,11 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
                                               float* __restrict__ weights,
                                               uint8_t* __restrict__ slot_of) {
     wave_priority_high();
-    constexpr int PER = 16;
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;  // uniform per wavefront
+    constexpr int PER = 4;
+    __shared__ uint64_t cand_key[64];
+    __shared__ float cand_sc[64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x;
     uint64_t key[PER];  // (order bits of s + bias) << 32 | ~e; 0 where the lane has no expert
     float sc[PER];
     // every logit and bias of this lane is loaded before the first use (clamped indices,
@@ -95,42 +101,64 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
     float lg[PER], bi[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int e = min(j * 64 + lane, E - 1);
+        const int e = min(j * 256 + wave * 64 + lane, E - 1);
         lg[j] = src[(size_t)t * E + e];
         bi[j] = bias[e];
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int e = j * 64 + lane;
+        const int e = j * 256 + wave * 64 + lane;
         const float s = sigmoid_defined(lg[j]);
         const bool live = e < E;
         sc[j] = live ? s : 0.0f;
         key[j] = live ? ((uint64_t)order_bits(__fadd_rn(s, bi[j])) << 32) | (uint32_t)~(uint32_t)e
                       : 0ull;
     }
-    float mine = 0.0f;  // lane k holds the score chosen for slot k
-    int my_id = 0;
+    // K rounds over this wavefront's keys: lane k ends with its slot-k winner (key, score)
+    uint64_t mine_key = 0;
+    float mine = 0.0f;
     for (int k = 0; k < K; ++k) {
         uint64_t best = 0;
 #pragma unroll
         for (int j = 0; j < PER; ++j) best = key[j] > best ? key[j] : best;
         best = wave_max64(best);
-        const uint32_t wl = (uint32_t)best;  // ~winner id: unique in the wavefront
-        const int win = (int)(~wl);          // uniform
-        const int owner = win & 63;
+        const uint32_t wl = (uint32_t)best;  // ~winner id (0 once the wavefront has no keys)
         // the owner lane drops the winning key and takes its score (matched by the unique
         // low word; no other lane matches)
         float sel = 0.0f;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const bool hit = (uint32_t)key[j] == wl;
+            const bool hit = best != 0ull && (uint32_t)key[j] == wl;
             sel = hit ? sc[j] : sel;
             key[j] = hit ? 0ull : key[j];
         }
+        const int owner = (int)(~wl) & 63;
         const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel), owner));
         if (lane == k) {
+            mine_key = best;
             mine = s_win;
-            my_id = win;
+        }
+    }
+    if (lane < 16) {
+        cand_key[wave * 16 + lane] = lane < K ? mine_key : 0ull;
+        cand_sc[wave * 16 + lane] = mine;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // the token's top-K among the 4K candidates (one a lane)
+    uint64_t ck = cand_key[lane];
+    const float cs = cand_sc[lane];
+    int my_id = 0;
+    mine = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const uint64_t best = wave_max64(ck);
+        const bool hit = ck == best;  // one lane: keys are unique and best is live
+        const int owner = (int)__builtin_ctzll(__ballot(hit));
+        ck = hit ? 0ull : ck;
+        const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), owner));
+        if (lane == k) {
+            mine = s_win;
+            my_id = (int)(~(uint32_t)best);
         }
     }
     float sum = 0.0f;
@@ -147,8 +175,8 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
 
 hipError_t launch_topk(int T, int E, int K, const float* logits, const float* bias, int renorm,
                        float scale, int32_t* ids, float* w, uint8_t* slot_of, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, T, E, K, logits, bias, renorm,
-                       scale, ids, w, slot_of);
+    hipLaunchKernelGGL(k_topk, dim3(T), dim3(256), 0, s, T, E, K, logits, bias, renorm, scale, ids,
+                       w, slot_of);
     return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // device memory, frees or synchronises; moe_layer keeps one side stream and two events
 // per device (created on its first call on that device) to run the shared expert beside
 // the routed path.
+#include <algorithm>
 #include <mutex>
 #include <string.h>
 
@@ -26,6 +27,8 @@ constexpr double kSideShareDown = 0.5;
 // planned for three quarters of the GPU it takes 4 splits of 128-token chunks, not 5
 // (measured 495.7 -> 487.2 us per layer at 256 tokens)
 constexpr double kFrontShare = 0.75;
+// past this many tokens the shared expert is forked after the routing lists (see moe_layer)
+constexpr int kLateForkTokens = 256;
 
 inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t up256(size_t b) { return (b + 255) / 256 * 256; }
@@ -102,7 +105,8 @@ Layout layout(const moe_dims* d) {
     for (size_t v : g2) us = v > us ? v : us;
     at += up256(us);
     lo.parts = at;
-    const size_t p1 = wgemm_parts_bytes(Tm, Ei + Li, Hi, kFrontShare),
+    const size_t p1 = std::max(wgemm_parts_bytes(Tm, Ei + Li, Hi, kFrontShare),
+                               wgemm_parts_bytes(Tm, Ei + Li, Hi, 1.0)),
                  p2 = wgemm_parts_bytes(Tm, Hi, Li);
     at += up256(p1 > p2 ? p1 : p2);
     lo.total = at;
@@ -441,26 +445,36 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     int s_fr = 1, s_gu = 1, s_sd = 1, s_up = 1;
     float* parts = (float*)(ws + lo.parts);
     float* parts_side = (float*)uni_side;
-    if (fast) {
-        // The shared expert depends on x only: its gate/up GEMM, activation, down GEMM and
-        // rounding run on the side stream ([wide] and [ep] module summaries: the shared
-        // expert beside the routed path), joined before the up-projection adds into it.
+    // The shared expert depends on x only: its gate/up GEMM, activation, down GEMM and
+    // rounding run on the side stream ([wide] and [ep] module summaries: the shared
+    // expert beside the routed path), joined before the up-projection adds into it.  Up to
+    // kLateForkTokens tokens it is forked at the start, beside the routing kernels; past
+    // that its GEMMs would fill every CU and starve them, so it is forked after the lists,
+    // beside the expert passes.
+    const bool late_fork = T > kLateForkTokens;
+    auto launch_side = [&]() -> bool {
         if (ss) {
-            MOE_TRY(hipEventRecord(ss->fork, s));
-            MOE_TRY(hipStreamWaitEvent(sh, ss->fork, 0));
+            if (hipEventRecord(ss->fork, s) != hipSuccess) return false;
+            if (hipStreamWaitEvent(sh, ss->fork, 0) != hipSuccess) return false;
         }
-        MOE_TRY(launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_gu, kSideShareGu));
-        MOE_TRY(launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh));
+        if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr, dpack,
+                         parts_side, sh, false, &s_gu, kSideShareGu) != hipSuccess)
+            return false;
+        if (launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh) != hipSuccess)
+            return false;
         // the down GEMM's split partials stay in the side scratch: the up-projection's
         // reduce adds them (shared rounded once to BF16) before it adds its own
-        MOE_TRY(launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_sd, kSideShareDown));
-        if (ss) MOE_TRY(hipEventRecord(ss->join, sh));
+        if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
+                         parts_side, sh, false, &s_sd, kSideShareDown) != hipSuccess)
+            return false;
+        return !ss || hipEventRecord(ss->join, sh) == hipSuccess;
+    };
+    if (fast) {
+        if (!late_fork && !launch_side()) return MOE_ERR_LAUNCH;
         // [wide] front: the router rows and the latent down rows as one FP32-out GEMM over
         // x; FP32 logits and the latent rounded once to BF16 from the same partials
         MOE_TRY(launch_wgemm(T, E + L, E, E + L, H, x, w->w_gate, w->w_down, nullptr, dpack, parts,
-                             s, true, &s_fr, kFrontShare));
+                             s, true, &s_fr, late_fork ? 1.0 : kFrontShare));
         // FP32 logits; the latent rounded once to BF16 and, for MXFP4 experts, its MXFP8
         // codes in the same pass
         if (mx)
@@ -491,6 +505,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
                         slot_of, s));
     MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, slot_of,
                          s));
+    if (fast && late_fork && !launch_side()) return MOE_ERR_LAUNCH;
     // MXFP8 latent, grouped experts, Finalize
     if (mx) {
         if (!fast) MOE_TRY(launch_quant_mxfp8(T, L, latent, codes, scales, s));

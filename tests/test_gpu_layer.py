@@ -2,7 +2,7 @@
 
 Toy latent MoE (T=8, BF16 experts): every output against the free-running oracle layer.
 Full layer (hidden 7168, latent 3584, 896 MXFP4 experts) at T=256 uniform and Zipf, and
-the sweep's T=65: every intermediate read from the documented workspace layout and
+the sweep's T=65 and T=510: every intermediate read from the documented workspace layout and
 checked teacher-forced -- each oracle step is fed the GPU's upstream outputs where a
 discrete decision follows (routing on the GPU's logits, quantisation on its latent, the
 experts on its codes and lists, Finalize on its rows): discrete results bit-exact,
@@ -43,7 +43,8 @@ def test_toy_layer(orc):
     assert_close_bf16(out, ref, "toy layer out")
 
 
-@pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False)])
+# T=510: past 256 tokens the shared expert is forked after the routing lists
+@pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False), (510, False)])
 def test_full_layer_teacher_forced(orc, T, zipf):
     say(f"full layer T={T} zipf={zipf}: generating weights")
     w, dw = full_weights(0, zipf)

@@ -217,6 +217,20 @@ __device__ __forceinline__ void load_token_ids(const int32_t* __restrict__ ids, 
 // bitmap below t).  A slot repeating an earlier slot's id is dropped, as in the marking.
 // Thread i owns tokens i, i + 1024, ...; the ids of its first token stay in registers
 // between the marking and the fill.
+// LDS of the one-workgroup build: bitmaps [W][E] u32, list offsets [E] u32, and -- when
+// the whole stays within kListsLds -- the per-word list positions [W][E] u16
+constexpr size_t kListsLds = 61440;
+__host__ __device__ inline size_t lists_base_lds(int T, int E) {
+    return ((size_t)(T + 31) / 32 * E + E) * sizeof(uint32_t);
+}
+__host__ __device__ inline bool lists_prefix_fits(int T, int E) {
+    return lists_base_lds(T, E) + (size_t)(T + 31) / 32 * E * sizeof(uint16_t) <= kListsLds;
+}
+static size_t lists_fused_lds(int T, int E) {
+    return lists_base_lds(T, E) +
+           (lists_prefix_fits(T, E) ? (size_t)(T + 31) / 32 * E * sizeof(uint16_t) : 0);
+}
+
 __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int unit,
                                                       const int32_t* __restrict__ ids,
                                                       int32_t* __restrict__ counts,
@@ -230,6 +244,10 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
     const int W = (T + 31) / 32;
     uint32_t* bm = lds_lists;                // [W][E]
     int* offl = (int*)(lds_lists + W * E);   // [E]
+    // with room for it, the list position of each (word, expert) before its own bits:
+    // pre[w][e] = offsets[e] + the set bits of e's words below w (< 2^16: T*K <= 65536)
+    uint16_t* pre = (uint16_t*)(offl + E);   // [W][E]
+    const bool use_pre = lists_prefix_fits(T, E);
     const int t0 = threadIdx.x;
     int32_t v0[16];
     if (t0 < T) load_token_ids(ids, t0, K, v0);
@@ -262,6 +280,13 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
     const int total_pairs = tot.x, touched = tot.y, later_total = tot.z;
     if (e < E) {
         offl[e] = off;
+        if (use_pre) {
+            int run = off;
+            for (int w = 0; w < W; ++w) {
+                pre[w * E + e] = (uint16_t)run;
+                run += __popc(bm[w * E + e]);
+            }
+        }
         counts[e] = c;
         offsets[e] = off;
         if (c > 0) units[fi] = make_int4(e, off, c < unit ? c : unit, c);
@@ -288,8 +313,13 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
 #pragma unroll
             for (int k2 = 0; k2 < k; ++k2) first = first && v[k2] != ek;
             if (!first) continue;
-            int pos = offl[ek] + __popc(bm[w * E + ek] & below);
-            for (int w2 = 0; w2 < w; ++w2) pos += __popc(bm[w2 * E + ek]);
+            int pos = __popc(bm[w * E + ek] & below);
+            if (use_pre) {
+                pos += pre[w * E + ek];
+            } else {
+                pos += offl[ek];
+                for (int w2 = 0; w2 < w; ++w2) pos += __popc(bm[w2 * E + ek]);
+            }
             pairs[pos] = t * K + k;
         }
     };
@@ -301,13 +331,8 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
     }
 }
 
-// LDS bytes of the one-workgroup build (bitmaps + list offsets); it runs when this is at
-// most 60 KiB and E <= 1024
-static size_t lists_fused_lds(int T, int E) {
-    return ((size_t)(T + 31) / 32 * E + E) * sizeof(uint32_t);
-}
-
-bool lists_fused_fits(int T, int E) { return E <= 1024 && lists_fused_lds(T, E) <= 61440; }
+// the one-workgroup build runs when its bitmaps and offsets fit in kListsLds, E <= 1024
+bool lists_fused_fits(int T, int E) { return E <= 1024 && lists_base_lds(T, E) <= kListsLds; }
 
 hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32_t* counts,
                         int32_t* offsets, int32_t* pairs, int32_t* units, int32_t* num_units,

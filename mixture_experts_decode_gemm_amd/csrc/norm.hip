@@ -162,10 +162,27 @@ __global__ __launch_bounds__(256) void k_silu_mul_parts(int M, int S8, int nspli
     const float4* gp = parts + m * ld4 + c * 2;     // 8 gate floats of this thread
     const float4* up = gp + S8 * 2;                 // 8 up floats
     float gv[8], uv[8];
+    // the loads of up to four splits go out together (one round trip, not one a split)
+    constexpr int MAXS = 4;
+    float4 ga[MAXS][2], ua[MAXS][2];
+#pragma unroll
+    for (int z = 0; z < MAXS; ++z)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            ga[z][h] = z < nsplit ? gp[z * zs + h] : make_float4(0.f, 0.f, 0.f, 0.f);
+            ua[z][h] = z < nsplit ? up[z * zs + h] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        float4 a = gp[h], b = up[h];
-        for (int z = 1; z < nsplit; ++z) {
+        float4 a = ga[0][h], b = ua[0][h];
+#pragma unroll
+        for (int z = 1; z < MAXS; ++z) {
+            if (z >= nsplit) break;
+            const float4 a2 = ga[z][h], b2 = ua[z][h];
+            a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+            b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+        }
+        for (int z = MAXS; z < nsplit; ++z) {
             const float4 a2 = gp[z * zs + h], b2 = up[z * zs + h];
             a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
             b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;

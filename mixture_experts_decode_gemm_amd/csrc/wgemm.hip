@@ -312,6 +312,23 @@ hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, cons
 // the front GEMM), columns [N0, N1) -> out1 (row stride N1 - N0) with MODE 0 FP32, 1 BF16
 // (one rounding), 2 BF16 of FP32(add1) + sum; columns from N1 on are left to another
 // consumer.  Four columns per thread; the S partials are added in split order.
+// Four columns of the S split partials (split stride zs floats) added in split order.  The
+// loads of up to eight splits are issued together, so the thread waits for one round
+// trip, not one per split.
+__device__ __forceinline__ v4f sum_splits(const float* __restrict__ p, size_t zs, int S) {
+    constexpr int MAXS = 8;
+    v4f q[MAXS];
+#pragma unroll
+    for (int zz = 0; zz < MAXS; ++zz)
+        q[zz] = zz < S ? *(const v4f*)(p + zz * zs) : (v4f){0.f, 0.f, 0.f, 0.f};
+    v4f v = q[0];
+#pragma unroll
+    for (int zz = 1; zz < MAXS; ++zz)
+        if (zz < S) v += q[zz];
+    for (int zz = MAXS; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
+    return v;
+}
+
 template <int MODE>
 __device__ __forceinline__ void store4(void* out, const void* add, size_t idx, v4f v) {
     if (MODE == 0) {
@@ -338,10 +355,7 @@ __global__ __launch_bounds__(256) void k_wg_reduce(int M, int N, int N0, int N1,
     const int n4 = N1 / 4;
     if (idx >= (long)M * n4) return;
     const int m = (int)(idx / n4), c = (int)(idx - (long)m * n4) * 4;
-    const size_t zs = (size_t)M * N;
-    const float* p = part + (size_t)m * N + c;
-    v4f v = *(const v4f*)p;
-    for (int zz = 1; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
+    const v4f v = sum_splits(part + (size_t)m * N + c, (size_t)M * N, S);
     if (c < N0)
         store4<0>(out0, nullptr, (size_t)m * N0 + c, v);
     else
@@ -374,12 +388,8 @@ __global__ __launch_bounds__(256) void k_wg_reduce_combine(int M, int N, int S,
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long)M * (N / 4)) return;
     const size_t zs = (size_t)M * N;
-    const float* p2 = part2 + idx * 4;
-    const float* p = part + idx * 4;
-    v4f a = *(const v4f*)p2;
-    v4f v = *(const v4f*)p;
-    for (int zz = 1; zz < S2; ++zz) a += *(const v4f*)(p2 + zz * zs);
-    for (int zz = 1; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
+    const v4f a = sum_splits(part2 + idx * 4, zs, S2);
+    v4f v = sum_splits(part + idx * 4, zs, S);
     const uint2 sh = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
     shared[idx] = sh;
     v[0] += bf16_lo(sh.x);
@@ -398,61 +408,67 @@ hipError_t launch_wg_reduce_combine(int M, int N, int S, const float* parts, int
 }
 
 // The front GEMM's reduce with the MXFP8 quantisation of the latent folded in: threads
-// below M * N0/4 add four logit columns each (FP32 out); each later thread owns one
-// 32-column block of one token's latent, adds its split partials in split order, rounds
-// them once to BF16 (the latent, written out) and writes the block's E4M3 codes and E8M0
-// scale.
+// below M * N0/4 add four logit columns each (FP32 out); each later thread owns eight
+// columns of one token's latent: it adds their split partials in split order, rounds them
+// once to BF16 (the latent, written out), and with the three other threads of its
+// 32-column block (neighbouring lanes: the block's amax by lane shuffles) writes the
+// block's E4M3 codes and E8M0 scale.
 __global__ __launch_bounds__(256) void k_wg_reduce_front(int M, int N, int N0, int N1, int S,
                                                          const float* __restrict__ part,
                                                          float* __restrict__ logits,
                                                          uint4* __restrict__ latent,
-                                                         uint4* __restrict__ codes,
+                                                         uint2* __restrict__ codes,
                                                          uint8_t* __restrict__ scales) {
     wave_priority_high();
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     const size_t zs = (size_t)M * N;
-    const long nlog = (long)M * (N0 / 4);
+    const long nlog = (long)M * (N0 / 4);  // a multiple of 8: blocks of four lanes align
     if (idx < nlog) {
         const int m = (int)(idx / (N0 / 4)), c = (int)(idx - (long)m * (N0 / 4)) * 4;
-        const float* p = part + (size_t)m * N + c;
-        v4f v = *(const v4f*)p;
-        for (int zz = 1; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
-        *(v4f*)(logits + (size_t)m * N0 + c) = v;
+        *(v4f*)(logits + (size_t)m * N0 + c) = sum_splits(part + (size_t)m * N + c, zs, S);
         return;
     }
-    const int cbs = (N1 - N0) / 32;
+    const int c8s = (N1 - N0) / 8;
     const long b = idx - nlog;
-    if (b >= (long)M * cbs) return;
-    const int m = (int)(b / cbs), cb = (int)(b - (long)m * cbs);
-    const float* p = part + (size_t)m * N + N0 + cb * 32;
-    v4f v[8];
+    if (b >= (long)M * c8s) return;  // whole blocks of four: (N1 - N0) % 32 == 0
+    const int m = (int)(b / c8s), c8 = (int)(b - (long)m * c8s);
+    const float* p = part + (size_t)m * N + N0 + c8 * 8;
+    const v4f v0 = sum_splits(p, zs, S), v1 = sum_splits(p + 4, zs, S);
+    const uint32_t q[4] = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                           pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+    latent[b] = make_uint4(q[0], q[1], q[2], q[3]);
+    uint32_t amax = 0;  // magnitude bits order like magnitudes for finite BF16
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = *(const v4f*)(p + 4 * i);
-    for (int zz = 1; zz < S; ++zz)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] += *(const v4f*)(p + zz * zs + 4 * i);
-    uint32_t q[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        q[2 * i] = pack_bf16x2(v[i][0], v[i][1]);
-        q[2 * i + 1] = pack_bf16x2(v[i][2], v[i][3]);
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = q[i] & 0x7FFFu, hi = (q[i] >> 16) & 0x7FFFu;
+        amax = amax > lo ? amax : lo;
+        amax = amax > hi ? amax : hi;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        latent[b * 4 + i] = make_uint4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
-    uint32_t out[8];
-    const int X = mxfp8_encode_block(q, out);
-    codes[b * 2] = make_uint4(out[0], out[1], out[2], out[3]);
-    codes[b * 2 + 1] = make_uint4(out[4], out[5], out[6], out[7]);
-    scales[b] = (uint8_t)(X + 127);
+    for (int off = 1; off < 4; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)amax, off, 64);
+        amax = amax > o ? amax : o;
+    }
+    const int X = mx_block_exponent(amax << 16);
+    uint32_t out[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t c0 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i]), -X));
+        const uint32_t c1 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i]), -X));
+        const uint32_t c2 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i + 1]), -X));
+        const uint32_t c3 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i + 1]), -X));
+        out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    codes[b] = make_uint2(out[0], out[1]);
+    if ((b & 3) == 0) scales[b >> 2] = (uint8_t)(X + 127);
 }
 
 hipError_t launch_wg_reduce_front(int M, int N, int N0, int N1, int S, const float* parts,
                                   float* logits, void* latent, uint8_t* codes, uint8_t* scales,
                                   hipStream_t s) {
-    const long n = (long)M * (N0 / 4) + (long)M * ((N1 - N0) / 32);
+    const long n = (long)M * (N0 / 4) + (long)M * ((N1 - N0) / 8);
     hipLaunchKernelGGL(k_wg_reduce_front, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M, N,
-                       N0, N1, S, parts, logits, (uint4*)latent, (uint4*)codes, scales);
+                       N0, N1, S, parts, logits, (uint4*)latent, (uint2*)codes, scales);
     return hipGetLastError();
 }
 

@@ -157,7 +157,7 @@ def main():
     # timed with HIP events on its launch stream and fed the layer's own codes, lists and
     # units; then the down pass and the whole grouped FFN the same way
     rows = torch.empty(T * 16, 3584, dtype=torch.bfloat16, device="cuda")
-    fws = torch.empty(moe.moe_ffn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    fws = torch.zeros(moe.moe_ffn_workspace_size(d), dtype=torch.uint8, device="cuda")
     ffn_w = (d, dw["w13"], dw["s13"], dw["w2"], dw["s2"])
     lists = (v["pairs"], v["units_raw"], v["num_units"])
 

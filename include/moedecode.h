@@ -157,7 +157,8 @@ moe_status moe_quant_mxfp8(int32_t rows, int32_t cols, const void* x, uint8_t* c
    windows (the first D units name the touched experts and their list lengths).
    workspace: >= moe_ffn_workspace_size(d) bytes; on return it holds the MXFP8 hidden of
    every listed pair: codes u8 [T*K, I] at offset 0 and E8M0 scales u8 [T*K, I/32] at
-   offset round_up(T*K*I, 256), indexed by pair id. */
+   offset round_up(T*K*I, 256), indexed by pair id; the 256 bytes after the scales hold
+   the two passes' work counters, which each call zeroes on its stream before use. */
 moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const void* act,
                            const uint8_t* act_scales, const int32_t* pairs,
                            const moe_unit* units, const int32_t* num_units, void* rows,
@@ -257,7 +258,7 @@ size_t moe_workspace_size(const moe_dims* d); /* bytes at d->max_tokens; 0 if d 
    11 rows bf16 [T*K,L], 12 routed bf16 [T,L], 13 shared bf16 [T,H], 14 normed bf16 [T,L],
    15 hidden codes u8 [T*K,I] (MXFP8 hidden of the experts, by pair id), 16 hidden scales
    u8 [T*K,I/32], 17 scratch (shared-expert intermediates, GEMM split partials, list
-   bitmaps).  Sizes are at d->max_tokens; the row-major tensors of a call with T tokens
+   bitmaps, the expert passes' work counters).  Sizes are at d->max_tokens; the row-major tensors of a call with T tokens
    occupy their first T rows. */
 #define MOE_WS_FIELDS 18
 moe_status moe_workspace_layout(const moe_dims* d, size_t offsets[MOE_WS_FIELDS]);

@@ -2,7 +2,7 @@
 
 Every source is compiled by hipcc with --offload-arch=gfx950 -O3 and the packed-FP32
 instructions disabled; router.hip (the bit-exact routing arithmetic) additionally with
--ffp-contract=off.  Objects go to _build/ next to this file; the library is linked into
+-ffp-contract=off, ffn.hip without the atomic optimizer.  Objects go to _build/ next to this file; the library is linked into
 this package directory.
 """
 import concurrent.futures as cf
@@ -22,7 +22,11 @@ SOURCES = ["abi.hip", "finalize.hip", "quant.hip", "router.hip", "lists.hip", "f
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", CSRC, "-I", INCLUDE]
-PER_FILE = {"router.hip": ["-ffp-contract=off"]}
+# ffn.hip: the expert passes take work tickets with one atomic add by one thread; the
+# atomic optimizer would turn it into a wave-wide add whose result is read at once (a wait
+# for every load in flight), so it is off there
+PER_FILE = {"router.hip": ["-ffp-contract=off"],
+            "ffn.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

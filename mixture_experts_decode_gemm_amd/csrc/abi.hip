@@ -64,7 +64,7 @@ moe_status check_dims(const moe_dims* d) {
 
 struct Layout {
     size_t off[MOE_WS_FIELDS];
-    size_t gu, act, uni, uni_side, parts, total;
+    size_t gu, act, uni, uni_side, parts, sync, total;
 };
 
 Layout layout(const moe_dims* d) {
@@ -109,6 +109,8 @@ Layout layout(const moe_dims* d) {
                                wgemm_parts_bytes(Tm, Ei + Li, Hi, 1.0)),
                  p2 = wgemm_parts_bytes(Tm, Hi, Li);
     at += up256(p1 > p2 ? p1 : p2);
+    lo.sync = at;  // the expert passes' work counters
+    at += 256;
     lo.total = at;
     return lo;
 }
@@ -260,11 +262,13 @@ moe_status moe_grouped_ffn_stages(const moe_dims* d, const moe_expert_weights* w
             return MOE_ERR_WORKSPACE;
         uint8_t* hid = (uint8_t*)workspace;
         uint8_t* hsc = hid + up256((size_t)d->tokens * d->top_k * d->expert_inter);
+        unsigned* counters =
+            (unsigned*)(hid + ffn_counter_offset(d->tokens * d->top_k, d->expert_inter));
         return launch_status(launch_ffn_mx(
             d->tokens, d->top_k, d->experts, d->latent, d->expert_inter, d->unit_tokens,
             (const uint8_t*)w->w13, (const uint8_t*)w->s13, (const uint8_t*)w->w2,
             (const uint8_t*)w->s2, (const uint8_t*)act, act_scales, pairs, (const int32_t*)units,
-            num_units, rows, hid, hsc, stages, packed, s));
+            num_units, rows, hid, hsc, stages, packed, counters, false, s));
     }
     return launch_status(launch_ffn_bf16(d->tokens, d->top_k, d->experts, d->latent,
                                          d->expert_inter, d->unit_tokens, w->w13, w->w2, act,
@@ -443,6 +447,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     if (ss) side_lock = std::unique_lock<std::mutex>(ss->mu);
     hipStream_t sh = ss ? ss->s : s;
     int s_fr = 1, s_gu = 1, s_sd = 1, s_up = 1;
+    unsigned* counters = (unsigned*)(ws + lo.sync);  // the expert passes' work counters
     float* parts = (float*)(ws + lo.parts);
     float* parts_side = (float*)uni_side;
     // The shared expert depends on x only: its gate/up GEMM, activation, down GEMM and
@@ -473,8 +478,9 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         if (!late_fork && !launch_side()) return MOE_ERR_LAUNCH;
         // [wide] front: the router rows and the latent down rows as one FP32-out GEMM over
         // x; FP32 logits and the latent rounded once to BF16 from the same partials
+        // (the GEMM also zeroes the expert passes' two work counters)
         MOE_TRY(launch_wgemm(T, E + L, E, E + L, H, x, w->w_gate, w->w_down, nullptr, dpack, parts,
-                             s, true, &s_fr, late_fork ? 1.0 : kFrontShare));
+                             s, true, &s_fr, late_fork ? 1.0 : kFrontShare, counters));
         // FP32 logits; the latent rounded once to BF16 and, for MXFP4 experts, its MXFP8
         // codes in the same pass
         if (mx)
@@ -512,7 +518,7 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_ffn_mx(T, K, E, L, I, d->unit_tokens, (const uint8_t*)w->experts.w13,
                               (const uint8_t*)w->experts.s13, (const uint8_t*)w->experts.w2,
                               (const uint8_t*)w->experts.s2, codes, scales, pairs, units, nu,
-                              rows, hid, hid_scales, 3, packed, s));
+                              rows, hid, hid_scales, 3, packed, counters, fast, s));
     } else {
         MOE_TRY(launch_ffn_bf16(T, K, E, L, I, d->unit_tokens, w->experts.w13, w->experts.w2,
                                 latent, pairs, units, nu, rows, s));

@@ -36,7 +36,15 @@ namespace moe {
 size_t ffn_scratch_bytes(int P, int I) {
     size_t codes = (size_t)P * I;
     size_t scales = (size_t)P * (I / 32);
-    return ((codes + 255) / 256) * 256 + ((scales + 255) / 256) * 256;
+    return ((codes + 255) / 256) * 256 + ((scales + 255) / 256) * 256 + 256;
+}
+
+// the expert passes' work counters (gate/up: 8 words, down: 8 words) in the last 256
+// bytes of that scratch
+size_t ffn_counter_offset(int P, int I) { return ffn_scratch_bytes(P, I) - 256; }
+
+__global__ void k_zero_words(unsigned* p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
 }
 
 __device__ __forceinline__ v8i load_fp4x32(const uint8_t* p) {
@@ -247,6 +255,7 @@ struct UpOut {
     size_t at;       // byte offset of the codes in hid (p * I + 32 j + c)
     size_t sat;      // byte offset of the scale in hid_scales
     bool ok, first;  // store at all; this lane holds c = 0
+    int ticket;      // the value thread 0 published through the epilogue's barrier
 };
 
 __device__ __forceinline__ void up_store(const UpOut& o, uint8_t* __restrict__ hid,
@@ -259,13 +268,15 @@ __device__ __forceinline__ void up_store(const UpOut& o, uint8_t* __restrict__ h
 
 __device__ __forceinline__ UpOut up_epilogue(const v4f (&acc)[4], float* __restrict__ red,
                                              bool store, int total, int n0, int pair, int j,
-                                             int I) {
+                                             int I, int* tick, int publish) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         *(v4f*)(red + (wave * 4 + m) * RED_TILE + r16 * 16 + 4 * g) = acc[m];
+    if (tick && threadIdx.x == 0) *tick = publish;
     lds_barrier();
+    const int ticket = tick ? *tick : 0;
     const int n = threadIdx.x >> 4, c = 2 * (threadIdx.x & 15);
     const int mg = c >> 4, cr = c & 15;
     float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
@@ -298,12 +309,13 @@ __device__ __forceinline__ UpOut up_epilogue(const v4f (&acc)[4], float* __restr
     o.sat = (size_t)p * (I / 32) + j;
     o.ok = store && n0 + n < total;
     o.first = c == 0;
+    o.ticket = ticket;
     return o;
 }
 
 template <int SPW>
 __device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, int n0, int I, bool store,
-                                          float* red) {
+                                          float* red, int* tick = nullptr, int publish = 0) {
     const int g = (threadIdx.x & 63) >> 4;
     v4f acc[4];
 #pragma unroll
@@ -317,7 +329,7 @@ __device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, int n0, int I, bool 
             acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), st.b[i], acc[m],
                                   (int)(st.ws[m][i] >> (8 * g)), sb);
     }
-    return up_epilogue(acc, red, store, st.un.w, n0, st.pair, st.j, I);
+    return up_epilogue(acc, red, store, st.un.w, n0, st.pair, st.j, I, tick, publish);
 }
 
 // All token groups of one item.  The first group's result is returned unstored (the
@@ -331,9 +343,10 @@ __device__ __forceinline__ UpOut up_compute(UpStage<SPW>& st, int K, int I, bool
                                             const int32_t* __restrict__ pairs,
                                             uint8_t* __restrict__ hid,
                                             uint8_t* __restrict__ hid_scales, float* red,
-                                            int& rb) {
+                                            int& rb, int* tick = nullptr, int publish = 0) {
     const int r16 = threadIdx.x & 15;
-    UpOut first = up_group(st, 0, I, store, red + rb * RED_FLOATS);
+    UpOut first = up_group(st, 0, I, store, red + rb * RED_FLOATS, tick ? tick + rb : nullptr,
+                           publish);
     rb ^= 1;
     if (st.un.w <= 16) return first;
     up_store(first, hid, hid_scales);
@@ -347,43 +360,89 @@ __device__ __forceinline__ UpOut up_compute(UpStage<SPW>& st, int K, int I, bool
     return first;
 }
 
+// Work order of both persistent passes: workgroup w takes the static items w, w + G, ...,
+// w + (2R - 1) G (R passes of two), then items from tickets as it frees up, so that
+// workgroups starting late (their CU still busy with the side stream's GEMMs) take fewer
+// of the last items instead of finishing late.  The dynamic tail is the last quarter of
+// the passes (at least two): the tickets' cost (an LDS round between a compute and the
+// next loads) is paid only there.  Items still go out in ascending order: the CUs sweep
+// one compact window of weights together.  Thread 0 takes each ticket one stage ahead --
+// just before the loads of the stage after the one it will name -- and publishes it
+// through the barrier of a later compute, so that neither a compute's wait for its own
+// loads nor the publishing waits for an atomic still in flight.  Tickets only grow, so a
+// workgroup's items ascend and the loop ends once one passes the count.
+// (at least two static passes before any ticket: the first tickets are taken in pass 0
+// for the items of pass 2; up to four passes everything is static)
+__device__ __forceinline__ int static_passes(int items, int G) {
+    const int passes = ((items + G - 1) / G + 1) / 2;
+    if (passes <= 4) return passes;
+    return passes - (passes / 4 > 2 ? passes / 4 : 2);
+}
+// One counter per XCD (workgroup w counts on counter w % 8, the XCD it is placed on), so
+// that each counter serves 1/8 of the workgroups; ticket t of counter x names item
+// base + 8t + x, base = 2RG (all counters together cover every item past the static ones
+// once).  With G < 8 some counters have no workgroup; callers launch G = min(items, CUs),
+// so then items = G and every item is static.
+__device__ __forceinline__ int take_ticket(unsigned* counters) {
+    return threadIdx.x == 0 ? (int)atomicAdd(counters + (blockIdx.x & 7), 1u) : 0;
+}
+__device__ __forceinline__ int ticket_item(int base, int t) { return base + 8 * t + (blockIdx.x & 7); }
+
 template <int SPW, bool PACKED>
 __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int K, int I, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
     const int32_t* __restrict__ num_units, uint8_t* __restrict__ hid,
-    uint8_t* __restrict__ hid_scales) {
+    uint8_t* __restrict__ hid_scales, unsigned* __restrict__ counter) {
     __shared__ __attribute__((aligned(16))) float red[2 * RED_FLOATS];
+    __shared__ int tick[2];
+    __shared__ int4 un_lds[1024];  // the first D units (one per touched expert), E <= 1024
     const int nt = I / UP_COLS;
-    const int items = num_units[2] * nt;  // touched experts x column tiles
+    const int D = num_units[2];
+    const int items = D * nt;  // touched experts x column tiles
     const int G = gridDim.x;
-    int item = blockIdx.x;
-    if (item >= items) return;
+    // the units in LDS: an item's unit is then an LDS read, not a global round trip
+    // between learning the item and issuing its weight loads
+    for (int i = threadIdx.x; i < D; i += 256) un_lds[i] = units[i];
+    __syncthreads();
+    int a = blockIdx.x;  // the item in stage A
+    if (a >= items) return;
+    int b = a + G;        // the item in stage B
+    const int R = static_passes(items, G), base = 2 * R * G;
+    int t_prev = 0;       // the ticket naming the next A (taken last pass, if dynamic)
     int rb = 0;
     UpStage<SPW> A, B;
-    up_issue_weights<SPW, PACKED>(A, item, nt, I, w13, s13, pairs, units);
+    up_issue_weights<SPW, PACKED>(A, a, nt, I, w13, s13, pairs, un_lds);
     up_issue_acts(A, K, codes, scales);
-    // Items in pairs (A = item, B = item + G).  Nothing between a stage's loads and its
-    // compute is conditional: a conditional exit there would let the compiler sink the
-    // loads below it, losing the prefetch.  Past the last item a stage repeats an item,
-    // computes it and stores nothing.
-    for (; item < items; item += 2 * G) {
-        const bool b_real = item + G < items;
+    // Items in pairs (stages A and B), pass k holding a_k and b_k.  Nothing between a
+    // stage's loads and its compute is conditional: a conditional exit there would let the
+    // compiler sink the loads below it, losing the prefetch.  Past the last item a stage
+    // repeats an item, computes it and stores nothing.
+    for (int k = 0;; ++k) {
+        const bool b_real = b < items;
+        const int t_b = k + 1 < R ? 0 : take_ticket(counter);  // names b_{k+1} if dynamic
         // (the scheduling barriers keep each stage's loads ahead of the other stage's
         // compute; otherwise the scheduler interleaves them into it)
-        up_issue_weights<SPW, PACKED>(B, b_real ? item + G : item, nt, I, w13, s13, pairs, units);
+        up_issue_weights<SPW, PACKED>(B, b_real ? b : a, nt, I, w13, s13, pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        const UpOut oa = up_compute(A, K, I, true, codes, scales, pairs, hid, hid_scales, red, rb);
+        const UpOut oa = up_compute(A, K, I, true, codes, scales, pairs, hid, hid_scales, red, rb,
+                                    tick, t_prev);
+        const int a_next = k + 1 < R ? a + 2 * G : ticket_item(base, oa.ticket);
         up_issue_acts(B, K, codes, scales);
-        const int na = item + 2 * G < items ? item + 2 * G : item;
-        up_issue_weights<SPW, PACKED>(A, na, nt, I, w13, s13, pairs, units);
+        t_prev = k + 2 < R ? 0 : take_ticket(counter);  // names a_{k+2} if dynamic
+        up_issue_weights<SPW, PACKED>(A, a_next < items ? a_next : a, nt, I, w13, s13, pairs,
+                                      un_lds);
         __builtin_amdgcn_sched_barrier(0);
         up_store(oa, hid, hid_scales);  // behind the loads just issued
-        const UpOut ob = up_compute(B, K, I, b_real, codes, scales, pairs, hid, hid_scales, red, rb);
+        const UpOut ob = up_compute(B, K, I, b_real, codes, scales, pairs, hid, hid_scales, red,
+                                    rb, tick, t_b);
         up_issue_acts(A, K, codes, scales);
         __builtin_amdgcn_sched_barrier(0);
         up_store(ob, hid, hid_scales);
+        if (a_next >= items) break;  // (every later item is larger)
+        b = k + 1 < R ? b + 2 * G : ticket_item(base, ob.ticket);
+        a = a_next;
     }
 }
 
@@ -573,30 +632,47 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     int L, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
     const uint8_t* __restrict__ hid, const uint8_t* __restrict__ hid_scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
-    const int32_t* __restrict__ num_units, uint16_t* __restrict__ rows) {
+    const int32_t* __restrict__ num_units, uint16_t* __restrict__ rows,
+    unsigned* __restrict__ counter) {
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][16 * (32 * MT + 16)];
+    __shared__ int tick[2];
+    __shared__ int4 un_lds[1024];  // the first D units, as in the up projection
     uint8_t* stage = stage_all[threadIdx.x >> 6];
     const int nt = L / (64 * MT);
-    const int items = num_units[2] * nt;
+    const int D = num_units[2];
+    const int items = D * nt;
     const int G = gridDim.x;
-    int item = blockIdx.x;
-    if (item >= items) return;
+    for (int i = threadIdx.x; i < D; i += 256) un_lds[i] = units[i];
+    __syncthreads();
+    int a = blockIdx.x;
+    if (a >= items) return;
+    int b = a + G;
+    const int R = static_passes(items, G), base = 2 * R * G;
+    int t_prev = 0;
     DownStage<IS, MT> A, B;
-    down_issue_weights<IS, MT, PACKED>(A, item, nt, L, w2, s2, pairs, units);
+    down_issue_weights<IS, MT, PACKED>(A, a, nt, L, w2, s2, pairs, un_lds);
     down_issue_acts(A, hid, hid_scales);
     // items in pairs, nothing conditional between a stage's loads and its compute (see
-    // the up projection)
-    for (; item < items; item += 2 * G) {
-        const bool b_real = item + G < items;
-        down_issue_weights<IS, MT, PACKED>(B, b_real ? item + G : item, nt, L, w2, s2, pairs,
-                                           units);
+    // the up projection); the dynamic tail's tickets as there, published through one
+    // barrier a stage
+    for (int k = 0;; ++k) {
+        const bool b_real = b < items;
+        const int t_b = k + 1 < R ? 0 : take_ticket(counter);
+        down_issue_weights<IS, MT, PACKED>(B, b_real ? b : a, nt, L, w2, s2, pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
         down_compute(A, L, true, hid, hid_scales, pairs, rows, stage);
+        int a_next = a + 2 * G;
+        if (k + 1 >= R) {  // uniform
+            if (threadIdx.x == 0) tick[0] = t_prev;
+            lds_barrier();
+            a_next = ticket_item(base, tick[0]);
+        }
         down_issue_acts(B, hid, hid_scales);
         const bool a_staged = A.un.w <= 16;
         const int a_j = A.j, a_pair = A.pair, a_w = A.un.w;
-        const int na = item + 2 * G < items ? item + 2 * G : item;
-        down_issue_weights<IS, MT, PACKED>(A, na, nt, L, w2, s2, pairs, units);
+        t_prev = k + 2 < R ? 0 : take_ticket(counter);
+        down_issue_weights<IS, MT, PACKED>(A, a_next < items ? a_next : a, nt, L, w2, s2, pairs,
+                                           un_lds);
         __builtin_amdgcn_sched_barrier(0);
         if (a_staged) {  // item A's deferred store, behind the loads just issued
             DownStage<IS, MT> done;
@@ -604,8 +680,17 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
             down_store(done, 0, L, true, rows, stage);
         }
         down_compute(B, L, b_real, hid, hid_scales, pairs, rows, stage);
+        int b_next = b + 2 * G;
+        if (k + 1 >= R) {
+            if (threadIdx.x == 0) tick[1] = t_b;
+            lds_barrier();
+            b_next = ticket_item(base, tick[1]);
+        }
         down_issue_acts(A, hid, hid_scales);
         if (B.un.w <= 16) down_store(B, 0, L, b_real, rows, stage);
+        if (a_next >= items) break;
+        a = a_next;
+        b = b_next;
     }
 }
 
@@ -686,9 +771,12 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const uint8_t* s13, const uint8_t* w2, const uint8_t* s2,
                          const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
                          const int32_t* units, const int32_t* num_units, void* rows,
-                         uint8_t* hid, uint8_t* hsc, int stages, bool packed, hipStream_t s) {
+                         uint8_t* hid, uint8_t* hsc, int stages, bool packed, unsigned* counters,
+                         bool counters_zeroed, hipStream_t s) {
     (void)T;
     (void)unit;
+    if (!counters_zeroed)
+        hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, counters, 16);
     const int4* un = (const int4*)units;
     const int up_items = E * (I / UP_COLS);  // an upper bound: the kernels read D on the device
     const int cus = num_cus();
@@ -701,10 +789,10 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     case SPW:                                                                                \
         if (packed)                                                                          \
             hipLaunchKernelGGL((k_ffn_up_fast<SPW, true>), ugrid, blk, 0, s, K, I, w13, s13, \
-                               codes, scales, pairs, un, num_units, hid, hsc);               \
+                               codes, scales, pairs, un, num_units, hid, hsc, counters);     \
         else                                                                                 \
             hipLaunchKernelGGL((k_ffn_up_fast<SPW, false>), ugrid, blk, 0, s, K, I, w13, s13,\
-                               codes, scales, pairs, un, num_units, hid, hsc);               \
+                               codes, scales, pairs, un, num_units, hid, hsc, counters);     \
         break;
         MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7)
 #undef MOE_UP
@@ -722,10 +810,12 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     case MT * 10 + IS:                                                                       \
         if (packed && MT == 8)                                                               \
             hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, true>), dgrid, blk, 0, s, L, w2, s2, \
-                               hid, hsc, pairs, un, num_units, (uint16_t*)rows);             \
+                               hid, hsc, pairs, un, num_units, (uint16_t*)rows,              \
+                               counters + 8);                                                \
         else                                                                                 \
             hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, false>), dgrid, blk, 0, s, L, w2, s2,\
-                               hid, hsc, pairs, un, num_units, (uint16_t*)rows);             \
+                               hid, hsc, pairs, un, num_units, (uint16_t*)rows,              \
+                               counters + 8);                                                \
         break;
         MOE_DOWN(8, 1) MOE_DOWN(8, 2) MOE_DOWN(8, 4) MOE_DOWN(4, 1) MOE_DOWN(4, 2)
         MOE_DOWN(4, 4)

@@ -37,7 +37,11 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const uint8_t* codes, const uint8_t* scales, const int32_t* pairs,
                          const int32_t* units, const int32_t* num_units, void* rows,
                          uint8_t* hid, uint8_t* hid_scales, int stages, bool packed,
-                         hipStream_t s);
+                         unsigned* counters, bool counters_zeroed, hipStream_t s);
+// counters: the two passes' work counters (16 words); counters_zeroed: the
+// caller's stream zeroed them since their last use (else the launcher zeroes them first
+// with a small kernel).  In moe_grouped_ffn's workspace they sit at ffn_counter_offset.
+size_t ffn_counter_offset(int P, int I);
 // the packed expert layout (see ffn.hip); L % 512 == 0, I / 128 in {1, 2, 4}
 hipError_t launch_pack_experts(int E, int L, int I, const uint8_t* w13, const uint8_t* s13,
                                const uint8_t* w2, const uint8_t* s2, uint8_t* pw13, uint8_t* ps13,
@@ -70,14 +74,15 @@ hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, i
 // is three row segments stacked: rows [0, N0) from w0, [N0, N1) from w1, [N1, N) from w2
 // (row-major, or packed by launch_pack_dense; empty segments may pass null); *S receives
 // the split count.  wgemm_fits tells whether the shape is supported (K % 128 == 0, every
-// segment a multiple of 32 rows, of 64 when packed, M * K < 2^31).
+// segment a multiple of 32 rows, of 64 when packed, M * K < 2^31).  zero (optional): 16
+// words the launch sets to 0, for the counters of a later launch on the same stream.
 bool wgemm_fits(int M, int N, int N0, int N1, int K, bool packed);
 // share: the fraction of the GPU the split plan assumes (1 when the GEMM runs alone)
 int wgemm_splits(int M, int N, int K, double share = 1.0);
 size_t wgemm_parts_bytes(int M, int N, int K, double share = 1.0);
 hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
                         const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
-                        bool prio, int* S, double share = 1.0);
+                        bool prio, int* S, double share = 1.0, unsigned* zero = nullptr);
 // adds the S partials (rows of stride N) in split order: columns [0, N0) to out0 (FP32),
 // [N0, N1) to out1 with mode1 0 FP32, 1 BF16, 2 BF16 of add1 + sum; columns past N1 untouched
 hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* parts, float* out0,

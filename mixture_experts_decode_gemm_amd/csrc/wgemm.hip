@@ -44,6 +44,7 @@ struct WgArgs {
     const uint16_t* x;     // [M, K] BF16
     const uint16_t* w[3];  // row segments [0, N0), [N0, N1), [N1, N): row-major or packed
     float* part;           // [S][M][N] FP32
+    unsigned* zero;        // optional: 16 words workgroup 0 sets to 0 (for a later launch)
     int M, K, N, N0, N1, S, NX, MCH, prio;  // M chunks of 32 * MT32 tokens
 };
 
@@ -69,6 +70,7 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
     if (a.prio) wave_priority_high();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (a.zero && blockIdx.x == 0 && tid < 16) a.zero[tid] = 0u;
     const int r32 = lane & 31, h = lane >> 5;
     // items: token chunk fastest, then weight tile, then K split -- the chunks of one
     // weight tile are neighbours on one XCD and share its weights through L2
@@ -285,9 +287,10 @@ static hipError_t launch_ks(const WgArgs& a, int mt32, bool packed, int G, hipSt
 
 hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
                         const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
-                        bool prio, int* S, double share) {
+                        bool prio, int* S, double share, unsigned* zero) {
     const WgPlan p = wg_plan(M, N, K, share);
     WgArgs a;
+    a.zero = zero;
     a.x = (const uint16_t*)x;
     a.w[0] = (const uint16_t*)w0;
     a.w[1] = (const uint16_t*)(w1 ? w1 : w0);

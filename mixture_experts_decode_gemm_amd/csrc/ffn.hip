@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
     const int32_t* __restrict__ num_units, uint8_t* __restrict__ hid,
-    uint8_t* __restrict__ hid_scales, unsigned* __restrict__ counter) {
+    uint8_t* __restrict__ hid_scales, unsigned* __restrict__ counter, int dyn) {
     __shared__ __attribute__((aligned(16))) float red[2 * RED_FLOATS];
     __shared__ int tick[2];
     __shared__ int4 un_lds[1024];  // the first D units (one per touched expert), E <= 1024
@@ -409,7 +409,8 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int a = blockIdx.x;  // the item in stage A
     if (a >= items) return;
     int b = a + G;        // the item in stage B
-    const int R = static_passes(items, G), base = 2 * R * G;
+    // dyn = 0: every pass static (no counter is touched)
+    const int R = dyn ? static_passes(items, G) : 0x7fffffff, base = dyn ? 2 * R * G : 0;
     int t_prev = 0;       // the ticket naming the next A (taken last pass, if dynamic)
     int rb = 0;
     UpStage<SPW> A, B;
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     const uint8_t* __restrict__ hid, const uint8_t* __restrict__ hid_scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
     const int32_t* __restrict__ num_units, uint16_t* __restrict__ rows,
-    unsigned* __restrict__ counter) {
+    unsigned* __restrict__ counter, int dyn) {
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][16 * (32 * MT + 16)];
     __shared__ int tick[2];
     __shared__ int4 un_lds[1024];  // the first D units, as in the up projection
@@ -647,7 +648,8 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     int a = blockIdx.x;
     if (a >= items) return;
     int b = a + G;
-    const int R = static_passes(items, G), base = 2 * R * G;
+    // dyn = 0: every pass static (no counter is touched)
+    const int R = dyn ? static_passes(items, G) : 0x7fffffff, base = dyn ? 2 * R * G : 0;
     int t_prev = 0;
     DownStage<IS, MT> A, B;
     down_issue_weights<IS, MT, PACKED>(A, a, nt, L, w2, s2, pairs, un_lds);
@@ -773,9 +775,9 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const int32_t* units, const int32_t* num_units, void* rows,
                          uint8_t* hid, uint8_t* hsc, int stages, bool packed, unsigned* counters,
                          bool counters_zeroed, hipStream_t s) {
-    (void)T;
     (void)unit;
-    if (!counters_zeroed)
+    const int dyn = T <= kDynTailTokens ? 1 : 0;
+    if (dyn && !counters_zeroed)
         hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, counters, 16);
     const int4* un = (const int4*)units;
     const int up_items = E * (I / UP_COLS);  // an upper bound: the kernels read D on the device
@@ -789,10 +791,10 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     case SPW:                                                                                \
         if (packed)                                                                          \
             hipLaunchKernelGGL((k_ffn_up_fast<SPW, true>), ugrid, blk, 0, s, K, I, w13, s13, \
-                               codes, scales, pairs, un, num_units, hid, hsc, counters);     \
+                               codes, scales, pairs, un, num_units, hid, hsc, counters, dyn);\
         else                                                                                 \
             hipLaunchKernelGGL((k_ffn_up_fast<SPW, false>), ugrid, blk, 0, s, K, I, w13, s13,\
-                               codes, scales, pairs, un, num_units, hid, hsc, counters);     \
+                               codes, scales, pairs, un, num_units, hid, hsc, counters, dyn);\
         break;
         MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7)
 #undef MOE_UP
@@ -811,11 +813,11 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
         if (packed && MT == 8)                                                               \
             hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, true>), dgrid, blk, 0, s, L, w2, s2, \
                                hid, hsc, pairs, un, num_units, (uint16_t*)rows,              \
-                               counters + 8);                                                \
+                               counters + 8, dyn);                                           \
         else                                                                                 \
             hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, false>), dgrid, blk, 0, s, L, w2, s2,\
                                hid, hsc, pairs, un, num_units, (uint16_t*)rows,              \
-                               counters + 8);                                                \
+                               counters + 8, dyn);                                           \
         break;
         MOE_DOWN(8, 1) MOE_DOWN(8, 2) MOE_DOWN(8, 4) MOE_DOWN(4, 1) MOE_DOWN(4, 2)
         MOE_DOWN(4, 4)

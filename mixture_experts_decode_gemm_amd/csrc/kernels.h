@@ -38,10 +38,13 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const int32_t* units, const int32_t* num_units, void* rows,
                          uint8_t* hid, uint8_t* hid_scales, int stages, bool packed,
                          unsigned* counters, bool counters_zeroed, hipStream_t s);
-// counters: the two passes' work counters (16 words); counters_zeroed: the
+// Up to kDynTailTokens tokens the passes end with a dynamic tail of work tickets (the
+// layer then runs the shared expert's GEMMs beside them; see moe_layer), else every pass
+// is static.  counters: the two passes' work counters (16 words); counters_zeroed: the
 // caller's stream zeroed them since their last use (else the launcher zeroes them first
 // with a small kernel).  In moe_grouped_ffn's workspace they sit at ffn_counter_offset.
 size_t ffn_counter_offset(int P, int I);
+constexpr int kDynTailTokens = 256;
 // the packed expert layout (see ffn.hip); L % 512 == 0, I / 128 in {1, 2, 4}
 hipError_t launch_pack_experts(int E, int L, int I, const uint8_t* w13, const uint8_t* s13,
                                const uint8_t* w2, const uint8_t* s2, uint8_t* pw13, uint8_t* ps13,

@@ -423,12 +423,15 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     for (int k = 0;; ++k) {
         const bool b_real = b < items;
         const int t_b = k + 1 < R ? 0 : take_ticket(counter);  // names b_{k+1} if dynamic
+        // tickets go through LDS only in the tail (a static pass reads none: its next items'
+        // addresses then wait for nothing)
+        int* const tk = k + 1 < R ? nullptr : tick;
         // (the scheduling barriers keep each stage's loads ahead of the other stage's
         // compute; otherwise the scheduler interleaves them into it)
         up_issue_weights<SPW, PACKED>(B, b_real ? b : a, nt, I, w13, s13, pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
         const UpOut oa = up_compute(A, K, I, true, codes, scales, pairs, hid, hid_scales, red, rb,
-                                    tick, t_prev);
+                                    tk, t_prev);
         const int a_next = k + 1 < R ? a + 2 * G : ticket_item(base, oa.ticket);
         up_issue_acts(B, K, codes, scales);
         t_prev = k + 2 < R ? 0 : take_ticket(counter);  // names a_{k+2} if dynamic
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
         __builtin_amdgcn_sched_barrier(0);
         up_store(oa, hid, hid_scales);  // behind the loads just issued
         const UpOut ob = up_compute(B, K, I, b_real, codes, scales, pairs, hid, hid_scales, red,
-                                    rb, tick, t_b);
+                                    rb, tk, t_b);
         up_issue_acts(A, K, codes, scales);
         __builtin_amdgcn_sched_barrier(0);
         up_store(ob, hid, hid_scales);

@@ -258,8 +258,8 @@ size_t moe_workspace_size(const moe_dims* d); /* bytes at d->max_tokens; 0 if d 
    11 rows bf16 [T*K,L], 12 routed bf16 [T,L], 13 shared bf16 [T,H], 14 normed bf16 [T,L],
    15 hidden codes u8 [T*K,I] (MXFP8 hidden of the experts, by pair id), 16 hidden scales
    u8 [T*K,I/32], 17 scratch (shared-expert intermediates, GEMM split partials, list
-   bitmaps, the expert passes' work counters).  Sizes are at d->max_tokens; the row-major tensors of a call with T tokens
-   occupy their first T rows. */
+   bitmaps, the expert passes' work counters).  Sizes are at d->max_tokens; the row-major
+   tensors of a call with T tokens occupy their first T rows. */
 #define MOE_WS_FIELDS 18
 moe_status moe_workspace_layout(const moe_dims* d, size_t offsets[MOE_WS_FIELDS]);
 

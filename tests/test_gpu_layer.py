@@ -133,3 +133,38 @@ def test_full_layer_dense_packed_equals_row_major(T):
     v, vr = moe.workspace_views(d, ws), moe.workspace_views(d, ws_ref)
     for k in ("logits", "latent", "shared"):
         assert torch.equal(v[k], vr[k]), k
+
+
+@pytest.mark.parametrize("zipf", [False, True])
+def test_full_layer_repeat_covers_every_pair(zipf):
+    """Two layer calls on one workspace give the same bytes, the second after the expert
+    rows and the MXFP8 hidden were overwritten with a NaN pattern: every listed pair's
+    row and hidden are rewritten by each call (the expert passes hand their last items
+    out by work tickets, so coverage depends on the counters being reset per call), and
+    a T=65 call in between leaves nothing behind that the next call depends on."""
+    _, dw = full_weights(0, zipf)
+    T = 256
+    x = syn.layer_input(syn.full_dims(T), seed=4)
+    d = moe.dims(T, 1020)
+    lw = moe.layer_weights(dw["w_gate"], dw["bias"], dw["w_down"], dw["w_shared_gu"],
+                           dw["w_shared_dn"], dw["norm_w"], dw["w_up"], dw["w13"], dw["s13"],
+                           dw["w2"], dw["s2"])
+    ws = torch.zeros(moe.moe_workspace_size(d), dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    out1 = torch.empty(T, d.hidden, dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer(d, lw, xd, out1, ws)
+    torch.cuda.synchronize()
+    v = moe.workspace_views(d, ws)
+    rows1, hid1, hsc1 = v["rows"].clone(), v["hidden"].clone(), v["hidden_scales"].clone()
+    d65 = moe.dims(65, 1020)
+    out65 = torch.empty(65, d.hidden, dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer(d65, lw, xd[:65].contiguous(), out65, ws)
+    for k in ("rows", "hidden", "hidden_scales"):
+        v[k].view(torch.uint8).fill_(0xFF)
+    out2 = torch.empty_like(out1)
+    moe.moe_layer(d, lw, xd, out2, ws)
+    torch.cuda.synchronize()
+    v = moe.workspace_views(d, ws)
+    assert torch.equal(v["rows"].view(torch.uint8), rows1.view(torch.uint8))
+    assert torch.equal(v["hidden"], hid1) and torch.equal(v["hidden_scales"], hsc1)
+    assert torch.equal(out2.view(torch.int16), out1.view(torch.int16))

@@ -108,7 +108,8 @@ Layout layout(const moe_dims* d) {
     lo.parts = at;
     const size_t p1 = std::max(wgemm_parts_bytes(Tm, Ei + Li, Hi, kFrontShare),
                                wgemm_parts_bytes(Tm, Ei + Li, Hi, 1.0)),
-                 p2 = wgemm_parts_bytes(Tm, Hi, Li);
+                 p2 = std::max(wgemm_parts_bytes(Tm, Hi, Li),
+                               wgemm_parts_bytes(Tm, Hi, Li, 1.0, true));
     at += up256(p1 > p2 ? p1 : p2);
     lo.sync = at;  // the expert passes' work counters
     at += 256;
@@ -532,10 +533,12 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_rmsnorm(T, L, routed, w->norm_w, d->rms_eps, normed, s));
     }
     // the up-projection added into the shared partial (one rounding); only its reduce
-    // needs the side stream's results
+    // needs the side stream's results.  With the shared expert forked early, the side
+    // stream is done by now and the GEMM has the GPU to itself (its plan counts its
+    // partials once); forked late, the side GEMMs may still run beside it.
     if (fast) {
         MOE_TRY(launch_wgemm(T, H, H, H, L, normed, w->w_up, nullptr, nullptr, dpack, parts, s,
-                             false, &s_up));
+                             false, &s_up, 1.0, nullptr, !late_fork));
         if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
         MOE_TRY(launch_wg_reduce_combine(T, H, s_up, parts, s_sd, parts_side, shared, out, s));
     } else {

@@ -196,7 +196,10 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
 // ---- plan ------------------------------------------------------------------------------
 // Split count from a cost model: the time is the larger of the MFMA time of the busiest
 // CU (rounds of workgroups) and the HBM time of the weights plus the split partials
-// (written, then read back by the reduce).  Rates are measured ones of this kernel on
+// (written, then read back by the reduce; counted once with parts_once, for a GEMM at the
+// end of the step whose reduce reads them right away with nothing else running: measured
+// on the up-projection at 256 tokens, 4 splits of 128-token chunks instead of 3 gain
+// 2 us a layer).  Rates are measured ones of this kernel on
 // MI355X: ~5 TFLOP/s per CU in its MFMA loop, ~5.5 TB/s of HBM traffic.  `share` is the
 // fraction of the GPU the GEMM is planned for (below 1 for a GEMM that runs beside
 // other work: fewer splits, fewer partial bytes).
@@ -210,7 +213,7 @@ struct WgPlan {
 // steps up to 256, 128-token steps past it) with one plan each.
 static int wg_class(int M) { return M <= 256 ? (M + 31) / 32 * 32 : (M + 127) / 128 * 128; }
 
-static WgPlan wg_plan(int M, int N, int K, double share) {
+static WgPlan wg_plan(int M, int N, int K, double share, bool parts_once) {
     const int KS = 64;  // (128-deep stages measured no faster at the layer's shapes)
     const int NX = (N + 255) / 256;
     const int Q = K / (2 * KS);
@@ -229,7 +232,7 @@ static WgPlan wg_plan(int M, int N, int K, double share) {
             const double rounds = (double)(long)((wgs + cus - 1) / cus);
             const double kz = (double)((Q + S - 1) / S) * 2 * KS;  // the longest K range
             const double t_mfma = rounds * 2.0 * 256 * (32.0 * mt32) * kz / rate;
-            const double t_hbm = (wbytes + 2.0 * S * Mc * N * 4) / bw;
+            const double t_hbm = (wbytes + (parts_once ? 1.0 : 2.0) * S * Mc * N * 4) / bw;
             const double t = t_mfma > t_hbm ? t_mfma : t_hbm;
             if (t < best * 0.995) {
                 best = t;
@@ -247,15 +250,17 @@ bool wgemm_fits(int M, int N, int N0, int N1, int K, bool packed) {
     return N0 % q == 0 && (N1 - N0) % q == 0 && (N - N1) % q == 0;
 }
 
-int wgemm_splits(int M, int N, int K, double share) { return wg_plan(M, N, K, share).S; }
+int wgemm_splits(int M, int N, int K, double share, bool parts_once) {
+    return wg_plan(M, N, K, share, parts_once).S;
+}
 
-size_t wgemm_parts_bytes(int M, int N, int K, double share) {
+size_t wgemm_parts_bytes(int M, int N, int K, double share, bool parts_once) {
     // the plan depends on M through the 32-token tile count and the 256-token chunks:
     // the largest M of each class bounds its partial buffer
     size_t best = 0;
     for (int m = 32;; m += (m < 256 ? 32 : 128)) {
         const int mm = m < M ? m : M;
-        const size_t b = (size_t)wg_plan(mm, N, K, share).S * mm * N * sizeof(float);
+        const size_t b = (size_t)wg_plan(mm, N, K, share, parts_once).S * mm * N * sizeof(float);
         if (b > best) best = b;
         if (m >= M) break;
     }
@@ -287,8 +292,8 @@ static hipError_t launch_ks(const WgArgs& a, int mt32, bool packed, int G, hipSt
 
 hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
                         const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
-                        bool prio, int* S, double share, unsigned* zero) {
-    const WgPlan p = wg_plan(M, N, K, share);
+                        bool prio, int* S, double share, unsigned* zero, bool parts_once) {
+    const WgPlan p = wg_plan(M, N, K, share, parts_once);
     WgArgs a;
     a.zero = zero;
     a.x = (const uint16_t*)x;

@@ -43,8 +43,10 @@ def test_toy_layer(orc):
     assert_close_bf16(out, ref, "toy layer out")
 
 
-# T=510: past 256 tokens the shared expert is forked after the routing lists
-@pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False), (510, False)])
+# T=510: past 256 tokens the shared expert is forked after the routing lists; T=130 and 192:
+# the up-projection's split plan runs 128-token chunks, the second one ragged
+@pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False), (510, False),
+                                    (130, False), (192, True)])
 def test_full_layer_teacher_forced(orc, T, zipf):
     say(f"full layer T={T} zipf={zipf}: generating weights")
     w, dw = full_weights(0, zipf)

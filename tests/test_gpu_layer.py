@@ -1,9 +1,9 @@
 """GPU parity of the whole layer (moe_layer) against the oracle.
 
 Toy latent MoE (T=8, BF16 experts): every output against the free-running oracle layer.
-Full layer (hidden 7168, latent 3584, 896 MXFP4 experts) at T=256 uniform and Zipf, and
-the sweep's T=65 and T=510: every intermediate read from the documented workspace layout and
-checked teacher-forced -- each oracle step is fed the GPU's upstream outputs where a
+Full layer (hidden 7168, latent 3584, 896 MXFP4 experts) at T=256 uniform and Zipf, the
+sweep's T=65, T=130 and T=510, and T=192 Zipf: every intermediate read from the documented
+workspace layout and checked teacher-forced -- each oracle step is fed the GPU's upstream outputs where a
 discrete decision follows (routing on the GPU's logits, quantisation on its latent, the
 experts on its codes and lists, Finalize on its rows): discrete results bit-exact,
 floating results within 2e-2 x RMS, Finalize exact; plus a free-running oracle layer on

@@ -38,7 +38,9 @@ def test_exp_defined_accuracy(orc):
         got = orc.exp_defined(float(z))
         ref = math.exp(float(z))
         worst = max(worst, abs(got - ref) / ulp32(ref))
-    assert worst <= 2.0, worst
+    # the defined steps land within one FP32 ulp of e^z (0.85 ulp measured); a dropped
+    # polynomial term or a wrong reduction constant lands beyond it (no r^7 term: 2.5 ulp)
+    assert worst <= 1.0, worst
     assert orc.exp_defined(0.0) == 1.0
 
 

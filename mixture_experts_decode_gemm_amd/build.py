@@ -47,7 +47,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    # only the C ABI's entry points are exported (the version script hides the rest)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs,
+           "-Wl,--version-script=" + os.path.join(CSRC, "exports.map"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

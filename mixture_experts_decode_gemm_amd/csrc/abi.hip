@@ -65,7 +65,7 @@ moe_status check_dims(const moe_dims* d) {
 
 struct Layout {
     size_t off[MOE_WS_FIELDS];
-    size_t gu, act, uni, uni_side, parts, sync, total;
+    size_t act, uni, uni_side, parts, sync, total;
 };
 
 Layout layout(const moe_dims* d) {
@@ -83,8 +83,6 @@ Layout layout(const moe_dims* d) {
         at += up256(sizes[i]);
     }
     lo.off[17] = at;
-    lo.gu = at;
-    at += up256(T * 2 * S * 2);
     lo.act = at;
     at += up256(T * S * 2);
     // scratch of the routed path (list bitmaps; the tiled GEMMs' split partials), of the
@@ -148,12 +146,6 @@ SideStream* side_stream() {
     return ss.ok ? &ss : nullptr;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* moe_version(void) { return "libmoedecode 0.1 (gfx950)"; }
-
 // the router GEMM: the weight-streaming kernel when the shape allows it
 bool router_fast(const moe_dims* d) {
     return wgemm_fits(d->max_tokens, d->experts, d->experts, d->experts, d->hidden, false);
@@ -163,6 +155,12 @@ size_t router_scratch(const moe_dims* d, int M) {
     return router_fast(d) ? wgemm_parts_bytes(M, d->experts, d->hidden)
                           : gemm_scratch_bytes(M, d->experts, d->hidden);
 }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "libmoedecode 0.1 (gfx950)"; }
 
 size_t moe_router_workspace_size(const moe_dims* d) {
     if (check_dims(d) != MOE_OK) return 0;
@@ -432,7 +430,6 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
     void* normed = ws + lo.off[14];
     uint8_t* hid = (uint8_t*)(ws + lo.off[15]);
     uint8_t* hid_scales = (uint8_t*)(ws + lo.off[16]);
-    void* gu = ws + lo.gu;
     void* act = ws + lo.act;
     void* uni = ws + lo.uni;
     void* uni_side = ws + lo.uni_side;

@@ -34,6 +34,20 @@ def test_exports_every_declared_entry_point(L):
     assert "gfx950" in moe.moe_version()
 
 
+def test_exports_nothing_undeclared(L):
+    """The library's dynamic symbol table holds exactly the header's entry points: every
+    kernel, launcher and helper stays internal."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    from mixture_experts_decode_gemm_amd import build
+    r = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
+                       text=True, check=True)
+    syms = sorted(line.split()[-1] for line in r.stdout.splitlines() if line.strip())
+    assert syms == header_entry_points()
+
+
 def good_dims(**kw):
     d = moe.dims(256, 1020)
     for k, v in kw.items():

@@ -201,8 +201,12 @@ def moe_quant_mxfp8(x, codes, scales, stream=None):
 
 
 def expert_weights(w13, s13, w2, s2):
-    return moe_expert_weights(_ptr(w13, (U8, BF16), "w13"), _ptr(s13, U8, "s13"),
-                              _ptr(w2, (U8, BF16), "w2"), _ptr(s2, U8, "s2"))
+    """The C struct of expert weight pointers; it holds the tensors, so that their memory
+    lives as long as the struct does."""
+    w = moe_expert_weights(_ptr(w13, (U8, BF16), "w13"), _ptr(s13, U8, "s13"),
+                           _ptr(w2, (U8, BF16), "w2"), _ptr(s2, U8, "s2"))
+    w._tensors = (w13, s13, w2, s2)
+    return w
 
 
 def moe_grouped_ffn(d, w13, s13, w2, s2, act, act_scales, pairs, units, num_units, rows,
@@ -288,11 +292,16 @@ def moe_silu_mul(gu, out, stream=None):
 
 def layer_weights(w_gate, bias, w_down, w_shared_gu, w_shared_down, norm_w, w_up, w13, s13, w2,
                   s2, dense_format=MOE_DENSE_ROWMAJOR):
-    return moe_layer_weights(_ptr(w_gate, BF16, "w_gate"), _ptr(bias, F32, "bias"),
-                             _ptr(w_down, BF16, "w_down"), _ptr(w_shared_gu, BF16, "w_shared_gu"),
-                             _ptr(w_shared_down, BF16, "w_shared_down"),
-                             _ptr(norm_w, BF16, "norm_w"), _ptr(w_up, BF16, "w_up"),
-                             expert_weights(w13, s13, w2, s2), int(dense_format))
+    """The C struct of layer weight pointers; it holds the tensors, so that their memory
+    lives as long as the struct does."""
+    ew = expert_weights(w13, s13, w2, s2)
+    lw = moe_layer_weights(_ptr(w_gate, BF16, "w_gate"), _ptr(bias, F32, "bias"),
+                           _ptr(w_down, BF16, "w_down"), _ptr(w_shared_gu, BF16, "w_shared_gu"),
+                           _ptr(w_shared_down, BF16, "w_shared_down"),
+                           _ptr(norm_w, BF16, "norm_w"), _ptr(w_up, BF16, "w_up"), ew,
+                           int(dense_format))
+    lw._tensors = (w_gate, bias, w_down, w_shared_gu, w_shared_down, norm_w, w_up, ew._tensors)
+    return lw
 
 
 def moe_layer(d, weights: moe_layer_weights, x, out, workspace, stream=None):
@@ -314,7 +323,7 @@ def workspace_views(d, workspace):
     return dict(logits=view("logits", T * E, F32, (T, E)), ids=view("ids", P, I32, (T, K)),
                 weights=view("weights", P, F32, (T, K)), counts=view("counts", E, I32, (E,)),
                 offsets=view("offsets", E + 1, I32, (E + 1,)), pairs=view("pairs", P, I32, (P,)),
-                num_units=view("num_units", 2, I32, (2,)),
+                num_units=view("num_units", 4, I32, (4,)),
                 latent=view("latent", T * L, BF16, (T, L)), codes=view("codes", T * L, U8, (T, L)),
                 scales=view("scales", T * L // 32, U8, (T, L // 32)),
                 rows=view("rows", P * L, BF16, (P, L)), routed=view("routed", T * L, BF16, (T, L)),

@@ -70,6 +70,7 @@ def _declare(L):
         "orc_silu_mul_bf16": (None, [i, i, v, v]),
         "orc_layer": (None, [C.POINTER(Dims), C.POINTER(Weights), v, v, C.POINTER(Trace)]),
         "orc_threads": (i, []),
+        "orc_set_threads": (None, [i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -129,6 +130,11 @@ def sigmoid_constants():
 
 def threads():
     return lib().orc_threads()
+
+
+def set_threads(n):
+    """Thread count of the oracle's parallel loops (for timing; results do not depend on it)."""
+    lib().orc_set_threads(int(n))
 
 
 # ---- steps ------------------------------------------------------------------------------

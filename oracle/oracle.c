@@ -37,6 +37,15 @@ int orc_threads(void) {
 #endif
 }
 
+/* thread count of the parallel loops (timing only: results do not depend on it) */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ============================ codecs ============================================= */
 
 float orc_bf16_to_f32(uint16_t b) {

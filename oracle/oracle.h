@@ -98,6 +98,7 @@ void orc_layer(const orc_dims* d, const orc_weights* w, const uint16_t* x, uint1
                orc_trace* trace);
 
 int orc_threads(void);
+void orc_set_threads(int n); /* thread count of the parallel loops; results do not depend on it */
 
 #ifdef __cplusplus
 }

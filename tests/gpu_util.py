@@ -122,24 +122,64 @@ def deq_mxfp4(packed, scales):
     return sh.reshape(v.shape)
 
 
+_E2M1_LUT = None
+
+
+def _mxfp4_rows(packed, scales):
+    """MXFP4 bytes [R, n/2] and E8M0 [R, n/32] of one expert -> FP64 [R, n] (byte lookup)."""
+    global _E2M1_LUT
+    if _E2M1_LUT is None:
+        b = np.arange(256)
+        _E2M1_LUT = np.stack([_E2M1[b & 15], _E2M1[b >> 4]], axis=-1)  # [256, 2]
+    v = _E2M1_LUT[packed].reshape(packed.shape[0], -1)
+    return (v.reshape(v.shape[0], -1, 32) * np.exp2(scales.astype(np.float64) - 127)[..., None]
+            ).reshape(v.shape)
+
+
 def hidden_error_bound(codes, scales, w13, s13, pairs, experts, K, I):
     """Per hidden element, a bound on |act_fp32 - act_exact| for any FP32 summation order
     of h = A W13^T: |dh| <= 64 * 2^-24 * sum_k |a_k w_k| for the gate and the up value,
-    propagated through silu(g) * u (plus one FP32 rounding of act)."""
+    propagated through silu(g) * u (plus one FP32 rounding of act).  Computed one expert
+    at a time (its weights dequantised once for all of its pairs)."""
+    pairs = np.asarray(pairs)
+    experts = np.asarray(experts)
     out = np.zeros((len(pairs), I))
     eps = 64 * 2.0 ** -24
-    for i, (p, e) in enumerate(zip(pairs, experts)):
-        a = deq_mxfp8(codes[p // K][None], scales[p // K][None])[0]
-        W = deq_mxfp4(w13[e], s13[e])
-        h = W @ a
-        S = np.abs(W) @ np.abs(a)
-        g, u = h[:I], h[I:]
+    for e in np.unique(experts):
+        sel = np.nonzero(experts == e)[0]
+        toks = pairs[sel] // K
+        A = torch.from_numpy(deq_mxfp8(codes[toks], scales[toks]))
+        W = torch.from_numpy(_mxfp4_rows(w13[e], s13[e]))
+        h = (A @ W.T).numpy()
+        S = (A.abs() @ W.abs().T).numpy()
+        g, u = h[:, :I], h[:, I:]
         sg = 1 / (1 + np.exp(-g))
         silu = g * sg
         dsilu = sg * (1 + g * (1 - sg))
-        out[i] = np.abs(dsilu * u) * eps * S[:I] + np.abs(silu) * eps * S[I:] + \
-            2.0 ** -23 * np.abs(silu * u)
+        out[sel] = (np.abs(dsilu * u) * eps * S[:, :I] + np.abs(silu) * eps * S[:, I:] +
+                    2.0 ** -23 * np.abs(silu * u))
     return out
+
+
+def mx_latent(orc, g, T, L):
+    """An MXFP8 latent quantised by the oracle from a BF16 latent N(0, 1) in which some
+    elements are scaled down by 2^-13 .. 2^-16 (their codes fall on the E4M3 subnormal
+    grid) and some blocks carry a largest element whose scaled value lies in [448, 512)
+    (it saturates to 448), so that every code class reaches the expert kernels."""
+    v = g.standard_normal((T, L)).astype(np.float32)
+    small = g.random((T, L)) < 1 / 16
+    v[small] *= np.exp2(-g.integers(13, 17, size=int(small.sum()))).astype(np.float32)
+    blocks = v.reshape(T, L // 32, 32)
+    sat = g.random((T, L // 32)) < 0.25
+    tt, bb = np.nonzero(sat)
+    j = g.integers(0, 32, size=len(tt))
+    mag = np.abs(blocks[tt, bb]).max(axis=1)
+    e = np.floor(np.log2(mag))
+    blocks[tt, bb, j] = np.float32(1.9375) * np.exp2(e + 1).astype(np.float32) * np.sign(
+        g.standard_normal(len(tt))).astype(np.float32)
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)
+    codes, scales = orc.quant_mxfp8_bf16(bits)
+    return codes, scales
 
 
 def check_hidden(got_codes, got_scales, ref_codes, ref_scales, act_exact, delta,

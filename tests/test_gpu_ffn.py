@@ -11,7 +11,7 @@ import torch
 import moe_synth as syn
 import mixture_experts_decode_gemm_amd as moe
 from gpu_util import (assert_close, assert_close_bf16, check_hidden, dev, f32,
-                      hidden_error_bound, host, say)
+                      hidden_error_bound, host, mx_latent, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,14 +68,18 @@ def check_mx(orc, d, w, codes, scales, ids, sample):
     assert_close(f32(rows[sample]), f32(ref), "rows (free-running oracle, sanity)", tol=0.1)
 
 
+# the last two shapes take the generic kernels: I = 384 (I / 128 = 3) the generic down pass,
+# L = 768 (not a multiple of 512) the generic gate/up pass and, with I = 640, the generic
+# down pass
 @pytest.mark.parametrize("T,K,E,L,I,unit", [(16, 4, 8, 512, 128, 8), (13, 3, 5, 256, 256, 16),
-                                            (1, 1, 3, 256, 128, 8)])
+                                            (1, 1, 3, 256, 128, 8), (24, 4, 6, 512, 384, 8),
+                                            (9, 2, 4, 768, 640, 8)])
 def test_ffn_mx_small(orc, T, K, E, L, I, unit):
     say(f"ffn mx T={T} K={K} E={E} L={L} I={I} unit={unit}")
     dd = dict(L=L, I=I, E=E, expert_format=0)
     w = syn.expert_weights(dd, seed=T)
     g = syn.rng(T, 700)
-    codes, scales = syn.mxfp8_random(g, T, L)
+    codes, scales = mx_latent(orc, g, T, L)
     ids = random_ids(np.random.default_rng(T), T, K, E)
     d = moe.dims(T, T, hidden=256, latent=L, experts=E, top_k=K, expert_inter=I,
                  unit_tokens=unit)
@@ -87,7 +91,7 @@ def test_ffn_mx_full_size_multi_unit(orc):
     say(f"ffn mx full T={T} K={K} E={E} L={L} I={I}")
     dd = dict(L=L, I=I, E=E, expert_format=0)
     w = syn.expert_weights(dd, seed=1)
-    codes, scales = syn.mxfp8_random(syn.rng(1, 701), T, L)
+    codes, scales = mx_latent(orc, syn.rng(1, 701), T, L)
     ids = random_ids(np.random.default_rng(5), T, K, E, hot=3)
     d = moe.dims(T, T)
     d.experts = E

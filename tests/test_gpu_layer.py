@@ -1,13 +1,17 @@
 """GPU parity of the whole layer (moe_layer) against the oracle.
 
 Toy latent MoE (T=8, BF16 experts): every output against the free-running oracle layer.
-Full layer (hidden 7168, latent 3584, 896 MXFP4 experts) at T=256 uniform and Zipf, the
-sweep's T=65, T=130 and T=510, and T=192 Zipf: every intermediate read from the documented
-workspace layout and checked teacher-forced -- each oracle step is fed the GPU's upstream outputs where a
-discrete decision follows (routing on the GPU's logits, quantisation on its latent, the
-experts on its codes and lists, Finalize on its rows): discrete results bit-exact,
-floating results within 2e-2 x RMS, Finalize exact; plus a free-running oracle layer on
-a few sampled tokens."""
+Full layer (hidden 7168, latent 3584, 896 MXFP4 experts) at every batch of the sweep
+(T = 65, 130, 255, 510, 1020 with uniform and Zipf routing; T = 256 and 192 besides):
+every intermediate read from the documented workspace layout and checked teacher-forced
+-- each oracle step is fed the GPU's upstream outputs where a discrete decision follows
+(routing on the GPU's logits, quantisation on its latent, the experts on its codes and
+lists, Finalize on its rows): discrete results bit-exact on every token, floating results
+within 2e-2 x RMS, Finalize exact; the projections and experts on sampled tokens, and at
+T=256 (uniform) on every token and every pair; plus a free-running oracle layer on a few
+sampled tokens."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -43,18 +47,29 @@ def test_toy_layer(orc):
     assert_close_bf16(out, ref, "toy layer out")
 
 
-# T=510: past 256 tokens the shared expert is forked after the routing lists; T=130 and 192:
-# the up-projection's split plan runs 128-token chunks, the second one ragged
-@pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False), (510, False),
-                                    (130, False), (192, True)])
-def test_full_layer_teacher_forced(orc, T, zipf):
-    say(f"full layer T={T} zipf={zipf}: generating weights")
+@functools.lru_cache(maxsize=2)
+def layer_run(T, zipf):
+    """One GPU layer call at T tokens of the full layer: (weights, x, out, intermediates)."""
     w, dw = full_weights(0, zipf)
-    d0 = syn.full_dims(T)
-    x = syn.layer_input(d0, seed=1)
+    x = syn.layer_input(syn.full_dims(T), seed=1)
     d = moe.dims(T, 1020)
     out, ws = run_layer(d, dw, x)
     v = {k: host(t) for k, t in moe.workspace_views(d, ws).items()}
+    del ws
+    return w, x, out, v
+
+
+# T=510 and 1020: past 256 tokens the shared expert is forked after the routing lists;
+# T=1020: the lists no longer fit one workgroup's LDS, so the top-K writes the slot map and
+# the three-launch list build reads it; T=130, 192 and 255: the up-projection's split plan
+# runs 128-token chunks, the second one ragged
+@pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False), (65, True),
+                                    (130, False), (192, True), (255, False), (510, False),
+                                    (510, True), (1020, False), (1020, True)])
+def test_full_layer_teacher_forced(orc, T, zipf):
+    say(f"full layer T={T} zipf={zipf}")
+    w, x, out, v = layer_run(T, zipf)
+    d0 = syn.full_dims(T)
     K, E = 16, 896
     rng = np.random.default_rng(T)
     toks = np.unique(np.r_[0, T - 1, rng.choice(T, 4, replace=False)])
@@ -67,6 +82,8 @@ def test_full_layer_teacher_forced(orc, T, zipf):
     assert np.array_equal(v["counts"], rl["counts"]) and np.array_equal(v["pairs"], rl["pairs"])
     assert v["num_units"][0] == rl["num_units"]
     assert np.array_equal(v["units_raw"][:rl["num_units"]], rl["units"])
+    assert np.array_equal(v["offsets"], rl["offsets"])
+    assert list(v["num_units"][:3]) == [rl["num_units"], rl["dropped"], rl["touched"]]
     D = int(np.count_nonzero(rl["counts"]))
     say(f"  D={D} touched experts, {rl['num_units']} units")
     # latent (sampled) and its MXFP8 codes (all tokens, on the GPU's latent)
@@ -102,6 +119,47 @@ def test_full_layer_teacher_forced(orc, T, zipf):
     d1 = dict(d0, T=len(sub))
     ref = orc.layer(d1, w, x[sub])
     assert_close(f32(out[sub]), f32(ref), "out (free-running oracle, sanity)", tol=0.1)
+
+
+def test_full_layer_every_pair_experts_T256(orc):
+    """T=256, uniform routing: the MXFP8 hidden and the expert row of EVERY (token, slot)
+    pair against the oracle fed the GPU's codes and lists (the expert passes hand their
+    last items out by work tickets at this size, so no item goes unchecked)."""
+    T, K = 256, 16
+    w, x, out, v = layer_run(T, False)
+    pairs = v["pairs"][:int(v["offsets"][-1])].astype(np.int32)
+    assert len(pairs) == T * K  # nothing dropped: every pair is listed
+    pexp = v["ids"].reshape(-1)[pairs]
+    say(f"  oracle gate/up pass on all {len(pairs)} pairs")
+    hc, hs, hf = orc.ffn_up_mx(pairs, pexp, K, v["codes"], v["scales"], w["w13"], w["s13"])
+    gh, gs = v["hidden"][pairs], v["hidden_scales"][pairs]
+    # the FP32 summation-error bound, only where a code or scale differs (an equal code is
+    # the rounding of the oracle's value and within half a step of it)
+    odd = np.nonzero(np.any(gh != hc, axis=1) | np.any(gs != hs, axis=1))[0]
+    delta = np.zeros(hf.shape)
+    if len(odd):
+        delta[odd] = hidden_error_bound(v["codes"], v["scales"], w["w13"], w["s13"], pairs[odd],
+                                        pexp[odd], K, 512)
+    say(f"  {len(odd)} pairs with a code that differs from the oracle's")
+    check_hidden(gh, gs, hc, hs, hf, delta)
+    say("  oracle down pass on all pairs (fed the GPU's hidden)")
+    rows_tf = orc.ffn_down_mx(pexp, gh, gs, w["w2"], w["s2"])
+    assert_close_bf16(v["rows"][pairs], rows_tf, "every expert row (oracle fed GPU hidden)")
+
+
+def test_full_layer_every_token_dense_T256(orc):
+    """T=256, uniform routing: logits, latent, shared expert and output of EVERY token
+    against the oracle (the output teacher-forced on the GPU's normed latent and shared)."""
+    T = 256
+    w, x, out, v = layer_run(T, False)
+    assert_close(v["logits"], orc.linear_f32(x, w["w_gate"]), "logits, every token")
+    assert_close_bf16(v["latent"], orc.linear_bf16(x, w["w_down"]), "latent, every token")
+    say("  oracle shared expert on every token")
+    gu = orc.linear_bf16(x, w["w_shared_gu"])
+    sh = orc.linear_bf16(orc.silu_mul_bf16(gu), w["w_shared_dn"])
+    assert_close_bf16(v["shared"], sh, "shared expert, every token")
+    o = orc.linear_add_bf16(v["normed"], w["w_up"], v["shared"])
+    assert_close_bf16(out, o, "out (teacher-forced), every token")
 
 
 def test_full_layer_packed_equals_row_major():

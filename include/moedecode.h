@@ -165,6 +165,26 @@ moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const
                            void* workspace, size_t ws_bytes, void* stream);
 size_t moe_ffn_workspace_size(const moe_dims* d);
 
+/* The grouped FFN above without a caller workspace, for callers that cannot allocate
+   device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+   allocation).  Same arguments, arithmetic and rows as moe_grouped_ffn; the MXFP8 hidden
+   and the work counters live in a device array of the library, of
+   moe_grouped_ffn_noalloc_max_bytes() bytes (9 MiB: 1020 tokens x top-16 at expert_inter
+   512), that every GPU the library runs on holds until the process ends.  The call
+   allocates nothing (no hipMalloc, no allocating library routine); on its first call on
+   a device it looks up the array's address there.  MOE_ERR_WORKSPACE when the call's
+   scratch (moe_ffn_workspace_size of these dims with max_tokens = tokens) exceeds the
+   array.  Every call on one
+   GPU shares that GPU's array: calls that overlap in time on one GPU (on different
+   streams, or from different host threads) race and must not be issued; calls on one
+   stream are ordered and safe.  The hidden left in the array is not part of the
+   interface. */
+moe_status moe_grouped_ffn_noalloc(const moe_dims* d, const moe_expert_weights* w,
+                                   const void* act, const uint8_t* act_scales,
+                                   const int32_t* pairs, const moe_unit* units,
+                                   const int32_t* num_units, void* rows, void* stream);
+size_t moe_grouped_ffn_noalloc_max_bytes(void);
+
 /* Load-time preparation of MXFP4 expert weights for the grouped FFN's loads (the pages
    prepare weights ahead of the decode step too: [wide] WideMoE prepares the layer's
    persistent experts for the wide batches, and [ep] pack_front packs the front GEMM's

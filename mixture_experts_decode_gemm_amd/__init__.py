@@ -53,7 +53,8 @@ class moe_layer_weights(C.Structure):
 
 
 EXPORTS = ["moe_router_topk", "moe_router_workspace_size", "moe_build_lists",
-           "moe_lists_workspace_size", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_stages", "moe_pack_expert_weights",
+           "moe_lists_workspace_size", "moe_quant_mxfp8", "moe_grouped_ffn", "moe_grouped_ffn_stages",
+           "moe_grouped_ffn_noalloc", "moe_grouped_ffn_noalloc_max_bytes", "moe_pack_expert_weights",
            "moe_ffn_workspace_size", "moe_finalize", "moe_rmsnorm", "moe_linear",
            "moe_linear_workspace_size", "moe_pack_dense_weight", "moe_silu_mul", "moe_layer",
            "moe_workspace_size",
@@ -81,6 +82,9 @@ def lib():
             "moe_grouped_ffn": (i32, [D, C.POINTER(moe_expert_weights), v, v, v, v, v, v, v, sz, v]),
             "moe_grouped_ffn_stages": (i32, [D, C.POINTER(moe_expert_weights), v, v, v, v, v, v, v,
                                              sz, i32, v]),
+            "moe_grouped_ffn_noalloc": (i32, [D, C.POINTER(moe_expert_weights), v, v, v, v, v, v,
+                                              v]),
+            "moe_grouped_ffn_noalloc_max_bytes": (sz, []),
             "moe_ffn_workspace_size": (sz, [D]),
             "moe_pack_expert_weights": (i32, [D, C.POINTER(moe_expert_weights),
                                               C.POINTER(moe_expert_weights), v]),
@@ -218,6 +222,22 @@ def moe_grouped_ffn(d, w13, s13, w2, s2, act, act_scales, pairs, units, num_unit
                                _ptr(rows, BF16, "rows"), _ptr(workspace, U8, "workspace"),
                                workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("moe_grouped_ffn", st)
+
+
+def moe_grouped_ffn_noalloc(d, w13, s13, w2, s2, act, act_scales, pairs, units, num_units, rows,
+                            stream=None):
+    """moe_grouped_ffn with its scratch in the library's own device array (no workspace)."""
+    w = expert_weights(w13, s13, w2, s2)
+    st = lib().moe_grouped_ffn_noalloc(C.byref(d), C.byref(w), _ptr(act, (U8, BF16), "act"),
+                                       _ptr(act_scales, U8, "act_scales"),
+                                       _ptr(pairs, I32, "pairs"), _ptr(units, I32, "units"),
+                                       _ptr(num_units, I32, "num_units"), _ptr(rows, BF16, "rows"),
+                                       _stream(stream))
+    _check("moe_grouped_ffn_noalloc", st)
+
+
+def moe_grouped_ffn_noalloc_max_bytes():
+    return lib().moe_grouped_ffn_noalloc_max_bytes()
 
 
 MOE_FFN_UP, MOE_FFN_DOWN = 1, 2

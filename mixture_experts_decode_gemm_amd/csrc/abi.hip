@@ -146,6 +146,32 @@ SideStream* side_stream() {
     return ss.ok ? &ss : nullptr;
 }
 
+// ---- the allocation-free grouped FFN -----------------------------------------------------
+// The grouped FFN's scratch (the MXFP8 hidden of every listed pair and the passes' work
+// counters) in a file-scope device array, for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy until the process ends.  In host code the array's
+// name is only a host-side stand-in: its device address, per device, comes from
+// hipGetSymbolAddress (taken on the entry point's first call on that device, with that
+// device current), and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = 9u << 20;  // 9 MiB: 1020 tokens x top-16 at I = 512
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+struct ScratchAddr {
+    std::once_flag once;
+    hipError_t err = hipErrorNotInitialized;
+    void* ptr = nullptr;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// the device address of `scratch` on the current device (nullptr if it cannot be had)
+void* scratch_addr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    ScratchAddr& sa = g_scratch[dev];
+    std::call_once(sa.once, [&] { sa.err = hipGetSymbolAddress(&sa.ptr, HIP_SYMBOL(scratch)); });
+    return sa.err == hipSuccess ? sa.ptr : nullptr;
+}
+
 // the router GEMM: the weight-streaming kernel when the shape allows it
 bool router_fast(const moe_dims* d) {
     return wgemm_fits(d->max_tokens, d->experts, d->experts, d->experts, d->hidden, false);
@@ -281,6 +307,24 @@ moe_status moe_grouped_ffn(const moe_dims* d, const moe_expert_weights* w, const
                            void* workspace, size_t ws_bytes, void* stream) {
     return moe_grouped_ffn_stages(d, w, act, act_scales, pairs, units, num_units, rows,
                                   workspace, ws_bytes, MOE_FFN_UP | MOE_FFN_DOWN, stream);
+}
+
+size_t moe_grouped_ffn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+moe_status moe_grouped_ffn_noalloc(const moe_dims* d, const moe_expert_weights* w,
+                                   const void* act, const uint8_t* act_scales,
+                                   const int32_t* pairs, const moe_unit* units,
+                                   const int32_t* num_units, void* rows, void* stream) {
+    const moe_status st = check_dims(d);
+    if (st != MOE_OK) return st;
+    // what this call uses: the MXFP8 hidden of its T*K pairs and the counters
+    if (d->expert_format != MOE_FMT_BF16 &&
+        ffn_scratch_bytes(d->tokens * d->top_k, d->expert_inter) > kNoAllocScratchBytes)
+        return MOE_ERR_WORKSPACE;
+    void* ws = scratch_addr();
+    if (!ws) return MOE_ERR_LAUNCH;
+    return moe_grouped_ffn_stages(d, w, act, act_scales, pairs, units, num_units, rows, ws,
+                                  kNoAllocScratchBytes, MOE_FFN_UP | MOE_FFN_DOWN, stream);
 }
 
 moe_status moe_pack_expert_weights(const moe_dims* d, const moe_expert_weights* src,

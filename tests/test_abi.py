@@ -48,6 +48,17 @@ def test_exports_nothing_undeclared(L):
     assert syms == header_entry_points()
 
 
+def test_noalloc_ffn_rejects_oversize_on_host(L):
+    """The allocation-free grouped FFN refuses, before any launch, a call whose scratch
+    exceeds its fixed device array (2048 tokens x top-16 x (512 + 16) bytes > 9 MiB)."""
+    d = moe.dims(2048, 2048)
+    w = moe.moe_expert_weights(FAKE, FAKE, FAKE, FAKE)
+    st = L.moe_grouped_ffn_noalloc(C.byref(d), C.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    assert L.moe_grouped_ffn_noalloc_max_bytes() == 9 << 20
+
+
 def good_dims(**kw):
     d = moe.dims(256, 1020)
     for k, v in kw.items():

@@ -160,7 +160,8 @@ def parse():
     p.add_argument("--zipf", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=192)
-    p.add_argument("--no-sweep", action="store_true", help="skip the 65..1020-token sweep")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the batch sweep (1..64 narrow batches and the 65..1020 wide ones)")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the Finalize, routing-front and copy-probe timings")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
@@ -363,7 +364,7 @@ def main():
         biases = {"uniform": dev(uniform_bias), "zipf": dev(zipf_bias)}  # (held while in use)
         for name in ("uniform", "zipf"):
             weights = lw_with(biases[name])
-            for t in (65, 130, 255, 256, 510, 1020):
+            for t in (1, 8, 32, 64, 65, 130, 255, 256, 510, 1020):
                 st = run_T(t, a.steps, 3, STAGE_FLOOR_S, weights)
                 m, Dt = st["ms"], st["D"]
                 bt = DENSE_BYTES + Dt * EXPERT_BYTES

@@ -218,6 +218,10 @@ static WgPlan wg_plan(int M, int N, int K, double share, bool parts_once) {
     const int NX = (N + 255) / 256;
     const int Q = K / (2 * KS);
     const double cus = gemm_device_cus() * share, rate = 5.0e12, bw = 5.5e12 * share;
+    // one workgroup streams weights at ~32 GB/s (the loads it keeps in flight over the
+    // loaded latency; measured on 36..48 workgroups at 8 tokens), so a plan with few
+    // workgroups cannot reach the HBM rate however small its partials are
+    const double bw_wg = 32e9;
     const double wbytes = (double)N * K * 2;
     // the class end bounds the partials: the plan is the same for every M of a class
     const double Mc = wg_class(M);
@@ -232,7 +236,9 @@ static WgPlan wg_plan(int M, int N, int K, double share, bool parts_once) {
             const double rounds = (double)(long)((wgs + cus - 1) / cus);
             const double kz = (double)((Q + S - 1) / S) * 2 * KS;  // the longest K range
             const double t_mfma = rounds * 2.0 * 256 * (32.0 * mt32) * kz / rate;
-            const double t_hbm = (wbytes + (parts_once ? 1.0 : 2.0) * S * Mc * N * 4) / bw;
+            const double active = wgs < cus ? wgs : cus;
+            const double rate_hbm = bw < active * bw_wg ? bw : active * bw_wg;
+            const double t_hbm = (wbytes + (parts_once ? 1.0 : 2.0) * S * Mc * N * 4) / rate_hbm;
             const double t = t_mfma > t_hbm ? t_mfma : t_hbm;
             if (t < best * 0.995) {
                 best = t;

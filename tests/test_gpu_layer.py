@@ -63,16 +63,19 @@ def layer_run(T, zipf):
 # T=1020: the lists no longer fit one workgroup's LDS, so the top-K writes the slot map and
 # the three-launch list build reads it; T=130, 192 and 255: the up-projection's split plan
 # runs 128-token chunks, the second one ragged
+# T=1..64: the narrow batches below the pages' wide range (one token; one unit window per
+# expert; ragged 32-token tiles)
 @pytest.mark.parametrize("T,zipf", [(256, False), (256, True), (65, False), (65, True),
                                     (130, False), (192, True), (255, False), (510, False),
-                                    (510, True), (1020, False), (1020, True)])
+                                    (510, True), (1020, False), (1020, True), (1, False),
+                                    (8, False), (32, True), (64, False)])
 def test_full_layer_teacher_forced(orc, T, zipf):
     say(f"full layer T={T} zipf={zipf}")
     w, x, out, v = layer_run(T, zipf)
     d0 = syn.full_dims(T)
     K, E = 16, 896
     rng = np.random.default_rng(T)
-    toks = np.unique(np.r_[0, T - 1, rng.choice(T, 4, replace=False)])
+    toks = np.unique(np.r_[0, T - 1, rng.choice(T, min(4, T), replace=False)])
     # router logits (sampled tokens) and routing on the GPU's logits (all tokens)
     assert_close(v["logits"][toks], orc.linear_f32(x[toks], w["w_gate"]), "logits")
     rid, rw = orc.topk(v["logits"], w["bias"], K, 1, 2.5)

@@ -119,6 +119,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// One 16-byte-per-lane direct load into LDS (the wavefront's 64 pieces land at dst +
+// 16 lane) from a raw buffer over [base, base + bytes); reads past the end return zeros.
+__device__ __forceinline__ void dma16(const void* base, int bytes, uint32_t off, lds_ptr dst) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+
 // 16-byte load marked non-temporal (the nt bit: the lines are streamed through the caches
 // with the lowest retention).  For weights that are read once per step: without it they
 // evict the small, re-read activations from L2 and those go back to HBM.

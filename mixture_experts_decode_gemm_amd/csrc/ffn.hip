@@ -163,13 +163,13 @@ __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t (&out)[N]
 // four 16-row tiles, with those steps' E8M0 scale bytes as dwords -- and applied to all
 // of the expert's tokens, 16 per MFMA column tile.  One workgroup per CU runs a software
 // pipeline: while item i is computed, the weights (and then the first activations) of
-// item i + gridDim are already in flight.
+// item i + gridDim are already in flight.  The activations of a token group go through
+// LDS (see up_issue_acts); their scale dwords are loaded into registers.
 template <int SPW>
 struct UpStage {
     uint4 w[4][SPW];        // FP4 weight fragments
     uint32_t ws[4][SPW];    // their scale dwords (byte g = K block 4s+g)
-    v8i b[SPW];             // FP8 activation fragments of the current token group
-    uint32_t bs[SPW];       // their scale dwords
+    uint32_t bs[SPW];       // the activations' scale dwords
     int4 un;                // (expert, list begin, window, list length)
     int j, pair;
 };
@@ -220,21 +220,44 @@ __device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int
     }
 }
 
+// The wavefront's activations for token group n0 (its SPW K steps of the group's 16
+// tokens) go to its own LDS area `act` (SPW x 2 KiB: step i at 2048 i, token r at 128 r,
+// its 16-byte chunk c at position c ^ (r & 7), so that the fragment reads of eight
+// consecutive tokens fall in distinct banks).  Direct loads bring eight whole 128-byte
+// token rows of a step per instruction (lane l: token l / 8, position l % 8), instead of
+// gathering the MFMA operand layout from sixteen half rows per instruction; the second
+// eight tokens are skipped when the group has at most eight.  A lane past the group's last
+// token holds a copy of a valid token: MFMA output column n depends on B column n only,
+// and such columns are never stored.  The scale dwords are register loads, issued last.
 template <int SPW>
-__device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int K,
-                                              const uint8_t* __restrict__ codes,
-                                              const uint8_t* __restrict__ scales) {
+__device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int K, int n0,
+                                              const uint8_t* __restrict__ codes, int cbytes,
+                                              const uint8_t* __restrict__ scales,
+                                              uint8_t* act) {
     constexpr int L = SPW * 512, SROW = L / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4;
-    // a lane past the group's last token holds a copy of a valid token: MFMA output
-    // column n depends on B column n only, and such columns are never stored
-    const int t = st.pair / K;
+    const int q = lane >> 3, pos = lane & 7;
+    // lane r (< 16) holds the pair of the group's token r
+    const uint32_t t0 = (uint32_t)(__shfl(st.pair, q, 64) / K);
+    const uint32_t t1 = (uint32_t)(__shfl(st.pair, 8 + q, 64) / K);
+    const uint32_t chunk = (uint32_t)((SPW * wave) * 128 + ((pos ^ q) << 4));
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
-        st.b[i] = load_fp8x32(codes + (size_t)t * L + (SPW * wave + i) * 128, g);
+        dma16(codes, cbytes, t0 * L + chunk + i * 128, (lds_ptr)(act + i * 2048));
+    if (st.un.w - n0 > 8) {  // (uniform)
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+            dma16(codes, cbytes, t1 * L + chunk + i * 128, (lds_ptr)(act + i * 2048 + 1024));
+    }
+    const int t = st.pair / K;
     load_dwords<SPW>(scales + (size_t)t * SROW + 4 * SPW * wave, st.bs);
 }
+
+// VMEM instructions of up_issue_weights (the pair id, SPW fragments and the scale dwords
+// of four tiles): a compute that follows the next item's weight issue waits with this
+// count for its own activations
+template <int SPW>
+constexpr int up_weight_loads() { return 1 + 4 * (SPW + SPW / 4 + (SPW % 4 ? 1 : 0)); }
 
 // Partial H tiles of the four wavefronts (each summed over its quarter of K), one buffer:
 // [wave][tile][token][row] FP32, tiles padded to 272 floats so that the gate and up reads
@@ -313,10 +336,26 @@ __device__ __forceinline__ UpOut up_epilogue(const v4f (&acc)[4], float* __restr
     return o;
 }
 
-template <int SPW>
-__device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, int n0, int I, bool store,
-                                          float* red, int* tick = nullptr, int publish = 0) {
-    const int g = (threadIdx.x & 63) >> 4;
+// NV: the VMEM instructions issued after the group's activations (their direct loads
+// are not tracked by the compiler, so the wait for them is explicit)
+template <int SPW, int NV>
+__device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, const uint8_t* act, int n0, int I,
+                                          bool store, float* red, int* tick = nullptr,
+                                          int publish = 0) {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    wait_vmcnt<NV>();
+    __builtin_amdgcn_sched_barrier(0);  // no fragment read moves above the wait
+    // B fragment of step i: token r16's bytes 16g.. and 64+16g.. of the step
+    const uint8_t* row = act + r16 * 128;
+    const int sw = r16 & 7;
+    v8i b[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const uint4 lo = *(const uint4*)(row + i * 2048 + ((g ^ sw) << 4));
+        const uint4 hi = *(const uint4*)(row + i * 2048 + (((4 + g) ^ sw) << 4));
+        b[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
     v4f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -326,35 +365,38 @@ __device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, int n0, int I, bool 
         const int sb = (int)(st.bs[i] >> (8 * g));
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), st.b[i], acc[m],
+            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][i]), b[i], acc[m],
                                   (int)(st.ws[m][i] >> (8 * g)), sb);
     }
     return up_epilogue(acc, red, store, st.un.w, n0, st.pair, st.j, I, tick, publish);
 }
 
 // All token groups of one item.  The first group's result is returned unstored (the
-// caller stores it after the next item's loads: stores and loads share one counter, so a
-// store issued before them would be waited for with them); later groups of a hot expert
-// are stored at once, and then the first group's too.
+// caller stores it, before the next activation loads); later groups of a hot expert are
+// stored at once, and then the first group's too.
+// The first group's activations are followed by the next item's weight issue (and at
+// most the conditional ticket, which is older and completes with them).
 template <int SPW>
 __device__ __forceinline__ UpOut up_compute(UpStage<SPW>& st, int K, int I, bool store,
-                                            const uint8_t* __restrict__ codes,
+                                            const uint8_t* __restrict__ codes, int cbytes,
                                             const uint8_t* __restrict__ scales,
                                             const int32_t* __restrict__ pairs,
                                             uint8_t* __restrict__ hid,
                                             uint8_t* __restrict__ hid_scales, float* red,
-                                            int& rb, int* tick = nullptr, int publish = 0) {
+                                            int& rb, uint8_t* act, int* tick = nullptr,
+                                            int publish = 0) {
     const int r16 = threadIdx.x & 15;
-    UpOut first = up_group(st, 0, I, store, red + rb * RED_FLOATS, tick ? tick + rb : nullptr,
-                           publish);
+    UpOut first = up_group<SPW, up_weight_loads<SPW>()>(
+        st, act, 0, I, store, red + rb * RED_FLOATS, tick ? tick + rb : nullptr, publish);
     rb ^= 1;
     if (st.un.w <= 16) return first;
     up_store(first, hid, hid_scales);
     first.ok = false;
     for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later token groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
-        up_issue_acts(st, K, codes, scales);
-        up_store(up_group(st, n0, I, store, red + rb * RED_FLOATS), hid, hid_scales);
+        up_issue_acts(st, K, n0, codes, cbytes, scales, act);
+        up_store(up_group<SPW, 0>(st, act, n0, I, store, red + rb * RED_FLOATS), hid,
+                 hid_scales);
         rb ^= 1;
     }
     return first;
@@ -391,13 +433,16 @@ __device__ __forceinline__ int ticket_item(int base, int t) { return base + 8 * 
 template <int SPW, bool PACKED>
 __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int K, int I, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint8_t* __restrict__ codes, int cbytes, const uint8_t* __restrict__ scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
     const int32_t* __restrict__ num_units, uint8_t* __restrict__ hid,
     uint8_t* __restrict__ hid_scales, unsigned* __restrict__ counter, int dyn) {
     __shared__ __attribute__((aligned(16))) float red[2 * RED_FLOATS];
     __shared__ int tick[2];
     __shared__ int4 un_lds[1024];  // the first D units (one per touched expert), E <= 1024
+    // each wavefront's activation area (one token group; see up_issue_acts)
+    __shared__ __attribute__((aligned(1024))) uint8_t act_all[4][SPW * 2048];
+    uint8_t* act = act_all[threadIdx.x >> 6];
     const int nt = I / UP_COLS;
     const int D = num_units[2];
     const int items = D * nt;  // touched experts x column tiles
@@ -415,11 +460,15 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int rb = 0;
     UpStage<SPW> A, B;
     up_issue_weights<SPW, PACKED>(A, a, nt, I, w13, s13, pairs, un_lds);
-    up_issue_acts(A, K, codes, scales);
+    up_issue_acts(A, K, 0, codes, cbytes, scales, act);
     // Items in pairs (stages A and B), pass k holding a_k and b_k.  Nothing between a
     // stage's loads and its compute is conditional: a conditional exit there would let the
     // compiler sink the loads below it, losing the prefetch.  Past the last item a stage
     // repeats an item, computes it and stores nothing.
+    // A stage's stores (conditional per lane) go out right after its compute, before the
+    // other stage's activation loads: a compute waits for its activations with a vmcnt
+    // that the compiler counts on the path without the stores, so stores issued after the
+    // activations would make that wait cover the first loads of the next item as well.
     for (int k = 0;; ++k) {
         const bool b_real = b < items;
         const int t_b = k + 1 < R ? 0 : take_ticket(counter);  // names b_{k+1} if dynamic
@@ -430,20 +479,22 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
         // compute; otherwise the scheduler interleaves them into it)
         up_issue_weights<SPW, PACKED>(B, b_real ? b : a, nt, I, w13, s13, pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        const UpOut oa = up_compute(A, K, I, true, codes, scales, pairs, hid, hid_scales, red, rb,
-                                    tk, t_prev);
+        const UpOut oa = up_compute(A, K, I, true, codes, cbytes, scales, pairs, hid, hid_scales,
+                                    red, rb, act, tk, t_prev);
         const int a_next = k + 1 < R ? a + 2 * G : ticket_item(base, oa.ticket);
-        up_issue_acts(B, K, codes, scales);
+        up_store(oa, hid, hid_scales);
+        __builtin_amdgcn_sched_barrier(0);
+        up_issue_acts(B, K, 0, codes, cbytes, scales, act);
         t_prev = k + 2 < R ? 0 : take_ticket(counter);  // names a_{k+2} if dynamic
         up_issue_weights<SPW, PACKED>(A, a_next < items ? a_next : a, nt, I, w13, s13, pairs,
                                       un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        up_store(oa, hid, hid_scales);  // behind the loads just issued
-        const UpOut ob = up_compute(B, K, I, b_real, codes, scales, pairs, hid, hid_scales, red,
-                                    rb, tk, t_b);
-        up_issue_acts(A, K, codes, scales);
-        __builtin_amdgcn_sched_barrier(0);
+        const UpOut ob = up_compute(B, K, I, b_real, codes, cbytes, scales, pairs, hid,
+                                    hid_scales, red, rb, act, tk, t_b);
         up_store(ob, hid, hid_scales);
+        __builtin_amdgcn_sched_barrier(0);
+        up_issue_acts(A, K, 0, codes, cbytes, scales, act);
+        __builtin_amdgcn_sched_barrier(0);
         if (a_next >= items) break;  // (every later item is larger)
         b = k + 1 < R ? b + 2 * G : ticket_item(base, ob.ticket);
         a = a_next;
@@ -609,10 +660,8 @@ __device__ __forceinline__ void down_store(const DownStage<IS, MT>& st, int n0, 
     }
 }
 
-// The item's first token group is computed and left staged (its store is issued by the
-// caller after the next item's loads, so that waiting for those loads never waits for
-// these stores: stores count in the same counter); later groups of a hot expert are
-// stored at once.
+// The item's first token group is computed and left staged (the caller stores it, before
+// the next activation loads); later groups of a hot expert are stored at once.
 template <int IS, int MT>
 __device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L, bool store,
                                              const uint8_t* __restrict__ hid,
@@ -657,9 +706,9 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     DownStage<IS, MT> A, B;
     down_issue_weights<IS, MT, PACKED>(A, a, nt, L, w2, s2, pairs, un_lds);
     down_issue_acts(A, hid, hid_scales);
-    // items in pairs, nothing conditional between a stage's loads and its compute (see
-    // the up projection); the dynamic tail's tickets as there, published through one
-    // barrier a stage
+    // items in pairs, nothing conditional between a stage's loads and its compute, each
+    // stage's stores right after its compute (see the up projection); the dynamic tail's
+    // tickets as there, published through one barrier a stage
     for (int k = 0;; ++k) {
         const bool b_real = b < items;
         const int t_b = k + 1 < R ? 0 : take_ticket(counter);
@@ -672,18 +721,13 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
             lds_barrier();
             a_next = ticket_item(base, tick[0]);
         }
+        if (A.un.w <= 16) down_store(A, 0, L, true, rows, stage);
+        __builtin_amdgcn_sched_barrier(0);
         down_issue_acts(B, hid, hid_scales);
-        const bool a_staged = A.un.w <= 16;
-        const int a_j = A.j, a_pair = A.pair, a_w = A.un.w;
         t_prev = k + 2 < R ? 0 : take_ticket(counter);
         down_issue_weights<IS, MT, PACKED>(A, a_next < items ? a_next : a, nt, L, w2, s2, pairs,
                                            un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        if (a_staged) {  // item A's deferred store, behind the loads just issued
-            DownStage<IS, MT> done;
-            done.j = a_j; done.pair = a_pair; done.un.w = a_w;
-            down_store(done, 0, L, true, rows, stage);
-        }
         down_compute(B, L, b_real, hid, hid_scales, pairs, rows, stage);
         int b_next = b + 2 * G;
         if (k + 1 >= R) {
@@ -691,8 +735,10 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
             lds_barrier();
             b_next = ticket_item(base, tick[1]);
         }
-        down_issue_acts(A, hid, hid_scales);
         if (B.un.w <= 16) down_store(B, 0, L, b_real, rows, stage);
+        __builtin_amdgcn_sched_barrier(0);
+        down_issue_acts(A, hid, hid_scales);
+        __builtin_amdgcn_sched_barrier(0);
         if (a_next >= items) break;
         a = a_next;
         b = b_next;
@@ -783,6 +829,7 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     if (dyn && !counters_zeroed)
         hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, counters, 16);
     const int4* un = (const int4*)units;
+    const int cbytes = T * L;  // the MXFP8 latent's codes (< 2^31: T <= 4096, L <= 3584)
     const int up_items = E * (I / UP_COLS);  // an upper bound: the kernels read D on the device
     const int cus = num_cus();
     const dim3 blk(256);
@@ -794,10 +841,12 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     case SPW:                                                                                \
         if (packed)                                                                          \
             hipLaunchKernelGGL((k_ffn_up_fast<SPW, true>), ugrid, blk, 0, s, K, I, w13, s13, \
-                               codes, scales, pairs, un, num_units, hid, hsc, counters, dyn);\
+                               codes, cbytes, scales, pairs, un, num_units, hid, hsc,        \
+                               counters, dyn);                                               \
         else                                                                                 \
             hipLaunchKernelGGL((k_ffn_up_fast<SPW, false>), ugrid, blk, 0, s, K, I, w13, s13,\
-                               codes, scales, pairs, un, num_units, hid, hsc, counters, dyn);\
+                               codes, cbytes, scales, pairs, un, num_units, hid, hsc,        \
+                               counters, dyn);                                               \
         break;
         MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7)
 #undef MOE_UP

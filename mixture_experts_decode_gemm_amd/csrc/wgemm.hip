@@ -113,13 +113,17 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
                 PACKED ? wsrc + (size_t)(k0 / 64 + q / 4) * 4096 + (q % 4) * 512
                        : wsrc + k0 + 16 * q);
     };
+    // activations through a raw buffer resource: the MUBUF form of the direct LDS load
+    // is counted on vmcnt alone (the FLAT form also counts as a pending LDS access, and
+    // the compiler then waits lgkmcnt(0) at every fragment read, exposing the LDS latency
+    // of the reads issued ahead)
+    const int xbytes = (int)min((long)a.M * a.K * 2, 0x7fffffffL);
     auto issue_a = [&](int slot, int st) {
         const int k0 = kb + min(st, nst - 1) * KS;
 #pragma unroll
         for (int i = 0; i < LA; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(a.x + asrc[i] + k0),
-                                             (lds_ptr)(lds + slot * SLOT + (i * 512 + wave * 64) * 16),
-                                             16, 0, 0);
+            dma16(a.x, xbytes, (asrc[i] + k0) * 2,
+                  (lds_ptr)(lds + slot * SLOT + (i * 512 + wave * 64) * 16));
     };
     v16f acc[MT32];
 #pragma unroll

@@ -517,6 +517,8 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
             return false;
         return !ss || hipEventRecord(ss->join, sh) == hipSuccess;
     };
+    // the routing slot map (for the list build past one workgroup), filled by the top-K
+    uint8_t* slot_of = lists_fused_fits(T, E) ? nullptr : lists_slot_map(uni, T, E);
     if (fast) {
         if (!late_fork && !launch_side()) return MOE_ERR_LAUNCH;
         // [wide] front: the router rows and the latent down rows as one FP32-out GEMM over
@@ -525,10 +527,12 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_wgemm(T, E + L, E, E + L, H, x, w->w_gate, w->w_down, nullptr, dpack, parts,
                              s, true, &s_fr, late_fork ? 1.0 : kFrontShare, counters));
         // FP32 logits; the latent rounded once to BF16 and, for MXFP4 experts, its MXFP8
-        // codes in the same pass
+        // codes in the same pass, with the sigmoid top-K of each token taken from its
+        // logits in LDS
         if (mx)
-            MOE_TRY(launch_wg_reduce_front(T, E + L, E, E + L, s_fr, parts, logits, latent, codes,
-                                           scales, s));
+            MOE_TRY(launch_front_topk(T, E + L, E, L, s_fr, parts, logits, w->bias, K,
+                                      d->renormalize, d->routed_scale, ids, wts, slot_of, latent,
+                                      codes, scales, s));
         else
             MOE_TRY(launch_wg_reduce(T, E + L, E, E + L, s_fr, parts, logits, 1, latent, nullptr,
                                      s, true));
@@ -548,10 +552,11 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_gemm(T, E, H, x, w->w_gate, logits, nullptr, 0, uni, s, 0, true));
         MOE_TRY(launch_gemm(T, L, H, x, w->w_down, latent, nullptr, 1, uni, s, 0, true));
     }
-    // sigmoid top-K, lists and unit windows
-    uint8_t* slot_of = lists_fused_fits(T, E) ? nullptr : lists_slot_map(uni, T, E);
-    MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts,
-                        slot_of, s));
+    // sigmoid top-K (already taken with the front reduce on the fast MXFP4 path), lists
+    // and unit windows
+    if (!(fast && mx))
+        MOE_TRY(launch_topk(T, E, K, logits, w->bias, d->renormalize, d->routed_scale, ids, wts,
+                            slot_of, s));
     MOE_TRY(launch_lists(T, K, E, d->unit_tokens, ids, counts, offs, pairs, units, nu, uni, slot_of,
                          s));
     if (fast && late_fork && !launch_side()) return MOE_ERR_LAUNCH;

@@ -87,6 +87,66 @@ __device__ __forceinline__ int mxfp8_encode_block(const uint32_t (&q)[16], uint3
     return X;
 }
 
+// Four columns of the S split partials (split stride zs floats) added in split order.  The
+// loads of up to eight splits are issued together, so the thread waits for one round
+// trip, not one per split.
+__device__ __forceinline__ v4f sum_splits(const float* __restrict__ p, size_t zs, int S) {
+    constexpr int MAXS = 8;
+    v4f q[MAXS];
+#pragma unroll
+    for (int zz = 0; zz < MAXS; ++zz)
+        q[zz] = zz < S ? *(const v4f*)(p + zz * zs) : (v4f){0.f, 0.f, 0.f, 0.f};
+    v4f v = q[0];
+#pragma unroll
+    for (int zz = 1; zz < MAXS; ++zz)
+        if (zz < S) v += q[zz];
+    for (int zz = MAXS; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
+    return v;
+}
+
+// One thread's share of the front GEMM's latent columns: eight consecutive columns b of
+// the M x (N1 - N0) latent (four threads per 32-column MXFP8 block) summed over the S split
+// partials in split order, rounded once to BF16 (latent), and the block's E4M3 codes and
+// E8M0 scale (the lanes of one block exchange their maxima; the first writes the scale).
+__device__ __forceinline__ void front_latent8(long b, int M, int N, int N0, int N1, int S,
+                                              const float* __restrict__ part,
+                                              uint4* __restrict__ latent,
+                                              uint2* __restrict__ codes,
+                                              uint8_t* __restrict__ scales) {
+    const int c8s = (N1 - N0) / 8;
+    const size_t zs = (size_t)M * N;
+    const int m = (int)(b / c8s), c8 = (int)(b - (long)m * c8s);
+    const float* p = part + (size_t)m * N + N0 + c8 * 8;
+    const v4f v0 = sum_splits(p, zs, S), v1 = sum_splits(p + 4, zs, S);
+    const uint32_t q[4] = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                           pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+    latent[b] = make_uint4(q[0], q[1], q[2], q[3]);
+    uint32_t amax = 0;  // magnitude bits order like magnitudes for finite BF16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = q[i] & 0x7FFFu, hi = (q[i] >> 16) & 0x7FFFu;
+        amax = amax > lo ? amax : lo;
+        amax = amax > hi ? amax : hi;
+    }
+#pragma unroll
+    for (int off = 1; off < 4; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)amax, off, 64);
+        amax = amax > o ? amax : o;
+    }
+    const int X = mx_block_exponent(amax << 16);
+    uint32_t out[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t c0 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i]), -X));
+        const uint32_t c1 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i]), -X));
+        const uint32_t c2 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i + 1]), -X));
+        const uint32_t c3 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i + 1]), -X));
+        out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    codes[b] = make_uint2(out[0], out[1]);
+    if ((b & 3) == 0) scales[b >> 2] = (uint8_t)(X + 127);
+}
+
 // ---- workgroup barrier over LDS only ----------------------------------------------------
 // __syncthreads() fences global memory too, which makes every wavefront wait for all of
 // its outstanding global loads (s_waitcnt vmcnt(0)) -- fatal to a software pipeline that

@@ -18,6 +18,14 @@ hipError_t launch_quant_mxfp8(int rows, int cols, const void* x, uint8_t* codes,
 hipError_t launch_topk(int T, int E, int K, const float* logits, const float* bias, int renorm,
                        float scale, int32_t* ids, float* w, uint8_t* slot_of, hipStream_t s);
 
+// the front GEMM's split partials [S][T][N] (router rows [0, E), latent rows [E, E + L)):
+// FP32 logits, sigmoid top-K as launch_topk, and the latent rounded once to BF16 with its
+// MXFP8 codes and scales (E % 4 == 0, E <= 1024, L % 32 == 0)
+hipError_t launch_front_topk(int T, int N, int E, int L, int S, const float* parts, float* logits,
+                             const float* bias, int K, int renorm, float scale, int32_t* ids,
+                             float* w, uint8_t* slot_of, void* latent, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s);
+
 // routing lists: scratch of lists_scratch_bytes(T, E) bytes, which ends with the slot map
 // (lists_slot_map) that launch_topk fills; slot_of null: the fill finds the slots in ids
 size_t lists_scratch_bytes(int T, int E);

@@ -83,32 +83,30 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
 // those of one top-K over all E keys.
 // slot_of (optional, [T][E] bytes): slot_of[t][e] = the slot that chose expert e, for
 // the list build (entries of experts a token did not choose are left as they are).
-__global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* __restrict__ src,
-                                              const float* __restrict__ bias, int renorm,
-                                              float scale, int32_t* __restrict__ ids,
-                                              float* __restrict__ weights,
-                                              uint8_t* __restrict__ slot_of) {
-    wave_priority_high();
+// lg: token t's E logits (global memory or LDS); cand_key, cand_sc: 64-entry LDS arrays
+__device__ __forceinline__ void topk_token(int t, int E, int K, const float* lg,
+                                           const float* __restrict__ bias, int renorm,
+                                           float scale, int32_t* __restrict__ ids,
+                                           float* __restrict__ weights,
+                                           uint8_t* __restrict__ slot_of, uint64_t* cand_key,
+                                           float* cand_sc) {
     constexpr int PER = 4;
-    __shared__ uint64_t cand_key[64];
-    __shared__ float cand_sc[64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x;
     uint64_t key[PER];  // (order bits of s + bias) << 32 | ~e; 0 where the lane has no expert
     float sc[PER];
     // every logit and bias of this lane is loaded before the first use (clamped indices,
     // no branches), so the wavefront waits for one round trip, not one per expert
-    float lg[PER], bi[PER];
+    float lgv[PER], bi[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = min(j * 256 + wave * 64 + lane, E - 1);
-        lg[j] = src[(size_t)t * E + e];
+        lgv[j] = lg[e];
         bi[j] = bias[e];
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = j * 256 + wave * 64 + lane;
-        const float s = sigmoid_defined(lg[j]);
+        const float s = sigmoid_defined(lgv[j]);
         const bool live = e < E;
         sc[j] = live ? s : 0.0f;
         key[j] = live ? ((uint64_t)order_bits(__fadd_rn(s, bi[j])) << 32) | (uint32_t)~(uint32_t)e
@@ -171,6 +169,65 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
         weights[(size_t)t * K + lane] = w;
         if (slot_of) slot_of[(size_t)t * E + my_id] = (uint8_t)lane;
     }
+}
+
+__global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* __restrict__ src,
+                                              const float* __restrict__ bias, int renorm,
+                                              float scale, int32_t* __restrict__ ids,
+                                              float* __restrict__ weights,
+                                              uint8_t* __restrict__ slot_of) {
+    wave_priority_high();
+    __shared__ uint64_t cand_key[64];
+    __shared__ float cand_sc[64];
+    topk_token(blockIdx.x, E, K, src + (size_t)blockIdx.x * E, bias, renorm, scale, ids, weights,
+               slot_of, cand_key, cand_sc);
+}
+
+// The front GEMM's split partials [S][T][N] (router rows [0, E), latent rows [E, E + L))
+// to routing and MXFP8 latent in one launch.  Workgroups [0, T): token t's E logits are
+// added over the splits in split order into LDS (and the logits array), then its top-K is
+// selected from LDS as k_topk does; the rest take the latent, eight columns a thread (see
+// front_latent8).  Saves the logits' round trip and a launch between the two steps.
+__global__ __launch_bounds__(256) void k_front_topk(int T, int N, int E, int L, int S,
+                                                    const float* __restrict__ part,
+                                                    float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int K,
+                                                    int renorm, float scale,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ weights,
+                                                    uint8_t* __restrict__ slot_of,
+                                                    uint4* __restrict__ latent,
+                                                    uint2* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
+    wave_priority_high();
+    __shared__ __attribute__((aligned(16))) float lg[1024];
+    __shared__ uint64_t cand_key[64];
+    __shared__ float cand_sc[64];
+    if ((int)blockIdx.x < T) {
+        const int t = blockIdx.x;
+        for (int c = threadIdx.x * 4; c < E; c += 1024) {
+            const v4f v = sum_splits(part + (size_t)t * N + c, (size_t)T * N, S);
+            *(v4f*)(lg + c) = v;
+            *(v4f*)(logits + (size_t)t * E + c) = v;
+        }
+        __syncthreads();
+        topk_token(t, E, K, lg, bias, renorm, scale, ids, weights, slot_of, cand_key, cand_sc);
+        return;
+    }
+    const long b = (long)(blockIdx.x - T) * 256 + threadIdx.x;
+    if (b >= (long)T * (L / 8)) return;
+    front_latent8(b, T, N, E, E + L, S, part, latent, codes, scales);
+}
+
+hipError_t launch_front_topk(int T, int N, int E, int L, int S, const float* parts, float* logits,
+                             const float* bias, int K, int renorm, float scale, int32_t* ids,
+                             float* w, uint8_t* slot_of, void* latent, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s) {
+    const long lat = ((long)T * (L / 8) + 255) / 256;
+    hipLaunchKernelGGL(k_front_topk, dim3((unsigned)(T + lat)), dim3(256), 0, s, T, N, E, L, S,
+                       parts, logits, bias, K, renorm, scale, ids, w, slot_of, (uint4*)latent,
+                       (uint2*)codes, scales);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(int T, int E, int K, const float* logits, const float* bias, int renorm,

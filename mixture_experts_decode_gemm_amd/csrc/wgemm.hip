@@ -330,23 +330,6 @@ hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, cons
 // the front GEMM), columns [N0, N1) -> out1 (row stride N1 - N0) with MODE 0 FP32, 1 BF16
 // (one rounding), 2 BF16 of FP32(add1) + sum; columns from N1 on are left to another
 // consumer.  Four columns per thread; the S partials are added in split order.
-// Four columns of the S split partials (split stride zs floats) added in split order.  The
-// loads of up to eight splits are issued together, so the thread waits for one round
-// trip, not one per split.
-__device__ __forceinline__ v4f sum_splits(const float* __restrict__ p, size_t zs, int S) {
-    constexpr int MAXS = 8;
-    v4f q[MAXS];
-#pragma unroll
-    for (int zz = 0; zz < MAXS; ++zz)
-        q[zz] = zz < S ? *(const v4f*)(p + zz * zs) : (v4f){0.f, 0.f, 0.f, 0.f};
-    v4f v = q[0];
-#pragma unroll
-    for (int zz = 1; zz < MAXS; ++zz)
-        if (zz < S) v += q[zz];
-    for (int zz = MAXS; zz < S; ++zz) v += *(const v4f*)(p + zz * zs);
-    return v;
-}
-
 template <int MODE>
 __device__ __forceinline__ void store4(void* out, const void* add, size_t idx, v4f v) {
     if (MODE == 0) {
@@ -446,39 +429,9 @@ __global__ __launch_bounds__(256) void k_wg_reduce_front(int M, int N, int N0, i
         *(v4f*)(logits + (size_t)m * N0 + c) = sum_splits(part + (size_t)m * N + c, zs, S);
         return;
     }
-    const int c8s = (N1 - N0) / 8;
     const long b = idx - nlog;
-    if (b >= (long)M * c8s) return;  // whole blocks of four: (N1 - N0) % 32 == 0
-    const int m = (int)(b / c8s), c8 = (int)(b - (long)m * c8s);
-    const float* p = part + (size_t)m * N + N0 + c8 * 8;
-    const v4f v0 = sum_splits(p, zs, S), v1 = sum_splits(p + 4, zs, S);
-    const uint32_t q[4] = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
-                           pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
-    latent[b] = make_uint4(q[0], q[1], q[2], q[3]);
-    uint32_t amax = 0;  // magnitude bits order like magnitudes for finite BF16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = q[i] & 0x7FFFu, hi = (q[i] >> 16) & 0x7FFFu;
-        amax = amax > lo ? amax : lo;
-        amax = amax > hi ? amax : hi;
-    }
-#pragma unroll
-    for (int off = 1; off < 4; off <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_xor((int)amax, off, 64);
-        amax = amax > o ? amax : o;
-    }
-    const int X = mx_block_exponent(amax << 16);
-    uint32_t out[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint32_t c0 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i]), -X));
-        const uint32_t c1 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i]), -X));
-        const uint32_t c2 = e4m3_rne_sat(ldexpf(bf16_lo(q[2 * i + 1]), -X));
-        const uint32_t c3 = e4m3_rne_sat(ldexpf(bf16_hi(q[2 * i + 1]), -X));
-        out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    }
-    codes[b] = make_uint2(out[0], out[1]);
-    if ((b & 3) == 0) scales[b >> 2] = (uint8_t)(X + 127);
+    if (b >= (long)M * ((N1 - N0) / 8)) return;  // whole blocks of four: (N1 - N0) % 32 == 0
+    front_latent8(b, M, N, N0, N1, S, part, latent, codes, scales);
 }
 
 hipError_t launch_wg_reduce_front(int M, int N, int N0, int N1, int S, const float* parts,

@@ -3,10 +3,10 @@
 // scale; wide page, WideRoute: an exact top-16 with renormalised weights).
 //
 // One workgroup of four wavefronts per token.  Each lane owns four experts (E <= 1024)
-// and builds 64-bit selection keys (order-preserving bits of the FP32 key s + bias, then
-// the complemented expert id so that equal keys prefer the lower id).  Rounds of a
-// wave-wide maximum (DPP, then readlane) pick winners in descending order, first within
-// each wavefront, then among the wavefronts' winners; the winner's lane clears its key.
+// and their 32-bit selection keys (order-preserving bits of the FP32 key s + bias).
+// Rounds of a wave-wide maximum (DPP, then readlane) pick winners in descending order,
+// first within each wavefront, then among the wavefronts' winners; a ballot names the
+// winner's lane, equal keys going to the lower expert id, and that lane clears its key.
 // Lane k keeps slot k's score; the slot-order FP32 sum, the divide and the routed scale
 // follow.
 //
@@ -52,47 +52,56 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide maximum of 64-bit keys, returned in every lane: DPP row shifts by 1, 2, 4, 8
+// Wave-wide maximum of 32-bit keys, uniform in every lane: DPP row shifts by 1, 2, 4, 8
 // leave each row's maximum in its lane 15, row broadcasts 15 and 31 carry them to lane 63,
 // and a readlane makes it uniform.  Lanes outside a shift's reach combine with 0, the
-// identity (every live key is nonzero).  The keys are compared as 64-bit integers (one
-// 64-bit compare and two selects a step, no scalar mask arithmetic).
+// identity (every live key is nonzero).
 template <int CTRL, int RMASK>
-__device__ __forceinline__ void dpp_max64(uint64_t& k) {
-    const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(k >> 32), CTRL, RMASK, 0xf, false);
-    const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, RMASK, 0xf, false);
-    const uint64_t o = ((uint64_t)h << 32) | l;
-    k = o > k ? o : k;
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t k) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, CTRL, RMASK, 0xf, false);
+    return o > k ? o : k;
 }
-__device__ __forceinline__ uint64_t wave_max64(uint64_t k) {
-    dpp_max64<0x111, 0xf>(k);  // row_shr:1
-    dpp_max64<0x112, 0xf>(k);  // row_shr:2
-    dpp_max64<0x114, 0xf>(k);  // row_shr:4
-    dpp_max64<0x118, 0xf>(k);  // row_shr:8
-    dpp_max64<0x142, 0xa>(k);  // row_bcast:15 into rows 1 and 3
-    dpp_max64<0x143, 0xc>(k);  // row_bcast:31 into rows 2 and 3
-    const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)(k >> 32), 63);
-    const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-    return ((uint64_t)h << 32) | l;
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t k) {
+    k = dpp_max_u32<0x111, 0xf>(k);  // row_shr:1
+    k = dpp_max_u32<0x112, 0xf>(k);  // row_shr:2
+    k = dpp_max_u32<0x114, 0xf>(k);  // row_shr:4
+    k = dpp_max_u32<0x118, 0xf>(k);  // row_shr:8
+    k = dpp_max_u32<0x142, 0xa>(k);  // row_bcast:15 into rows 1 and 3
+    k = dpp_max_u32<0x143, 0xc>(k);  // row_bcast:31 into rows 2 and 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)k, 63);
+}
+
+// The lane that wins a round: of the lanes whose candidate key equals the wave maximum,
+// the only one, or -- equal FP32 keys, rare -- the one whose candidate has the lowest
+// expert id (the maximum of ~e over the tied lanes; ids are unique).
+__device__ __forceinline__ int winner_lane(bool hit, int cand_e) {
+    const uint64_t bal = __ballot(hit);
+    if (__popcll(bal) == 1) return (int)__builtin_ctzll(bal);  // (uniform)
+    const uint32_t ne = hit ? ~(uint32_t)cand_e : 0u;
+    const uint32_t m = wave_max_u32_dpp(ne);
+    return (int)__builtin_ctzll(__ballot(hit && ne == m));
 }
 
 // One 256-thread workgroup per token.  Wavefront w owns experts w*64 + lane + 256 j
-// (j < 4, E <= 1024) and finds its own top-K in K rounds (its K winners, keys and scores,
-// to LDS); wavefront 0 then takes the 4K candidates, one a lane, and picks the token's
-// top-K from them in K more rounds.  Keys are unique, so the winners and their order are
-// those of one top-K over all E keys.
+// (j < 4, E <= 1024) with keys = order bits of the FP32 s + bias (0 where the lane has no
+// expert).  It finds its own top-K in K rounds: each lane offers its best remaining key
+// (the lowest j among equal ones), a 32-bit wave maximum names the winning key, a ballot
+// its lane (ties between lanes go to the lowest expert id), and the winner drops it.  Its K
+// winners (key, id, score) go to LDS; wavefront 0 then takes the 4K candidates, one a lane,
+// and picks the token's top-K from them the same way.  The order is that of one top-K over
+// all E keys: descending key, equal keys by ascending expert id.
+// lg: token t's E logits (global memory or LDS); cand_*: 64-entry LDS arrays.
 // slot_of (optional, [T][E] bytes): slot_of[t][e] = the slot that chose expert e, for
 // the list build (entries of experts a token did not choose are left as they are).
-// lg: token t's E logits (global memory or LDS); cand_key, cand_sc: 64-entry LDS arrays
 __device__ __forceinline__ void topk_token(int t, int E, int K, const float* lg,
                                            const float* __restrict__ bias, int renorm,
                                            float scale, int32_t* __restrict__ ids,
                                            float* __restrict__ weights,
-                                           uint8_t* __restrict__ slot_of, uint64_t* cand_key,
-                                           float* cand_sc) {
+                                           uint8_t* __restrict__ slot_of, uint32_t* cand_key,
+                                           int* cand_e, float* cand_sc) {
     constexpr int PER = 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t key[PER];  // (order bits of s + bias) << 32 | ~e; 0 where the lane has no expert
+    uint32_t key[PER];
     float sc[PER];
     // every logit and bias of this lane is loaded before the first use (clamped indices,
     // no branches), so the wavefront waits for one round trip, not one per expert
@@ -109,54 +118,59 @@ __device__ __forceinline__ void topk_token(int t, int E, int K, const float* lg,
         const float s = sigmoid_defined(lgv[j]);
         const bool live = e < E;
         sc[j] = live ? s : 0.0f;
-        key[j] = live ? ((uint64_t)order_bits(__fadd_rn(s, bi[j])) << 32) | (uint32_t)~(uint32_t)e
-                      : 0ull;
+        key[j] = live ? order_bits(__fadd_rn(s, bi[j])) : 0u;
     }
-    // K rounds over this wavefront's keys: lane k ends with its slot-k winner (key, score)
-    uint64_t mine_key = 0;
+    // K rounds over this wavefront's keys: lane k ends with its slot-k winner
+    uint32_t mine_key = 0;
+    int mine_e = 0;
     float mine = 0.0f;
     for (int k = 0; k < K; ++k) {
-        uint64_t best = 0;
+        uint32_t c = key[0];
+        int jc = 0;
+        float cs = sc[0];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) best = key[j] > best ? key[j] : best;
-        best = wave_max64(best);
-        const uint32_t wl = (uint32_t)best;  // ~winner id (0 once the wavefront has no keys)
-        // the owner lane drops the winning key and takes its score (matched by the unique
-        // low word; no other lane matches)
-        float sel = 0.0f;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const bool hit = best != 0ull && (uint32_t)key[j] == wl;
-            sel = hit ? sc[j] : sel;
-            key[j] = hit ? 0ull : key[j];
+        for (int j = 1; j < PER; ++j) {
+            const bool better = key[j] > c;  // strict: equal keys keep the lower j
+            c = better ? key[j] : c;
+            jc = better ? j : jc;
+            cs = better ? sc[j] : cs;
         }
-        const int owner = (int)(~wl) & 63;
-        const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel), owner));
+        const uint32_t M = wave_max_u32_dpp(c);
+        if (M == 0u) break;  // (uniform) the wavefront has no keys left
+        const int ce = jc * 256 + wave * 64 + lane;
+        const int wl = winner_lane(c == M, ce);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) key[j] = (lane == wl && j == jc) ? 0u : key[j];
+        const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), wl));
+        const int e_win = __builtin_amdgcn_readlane(ce, wl);
         if (lane == k) {
-            mine_key = best;
+            mine_key = M;
+            mine_e = e_win;
             mine = s_win;
         }
     }
     if (lane < 16) {
-        cand_key[wave * 16 + lane] = lane < K ? mine_key : 0ull;
+        cand_key[wave * 16 + lane] = lane < K ? mine_key : 0u;
+        cand_e[wave * 16 + lane] = mine_e;
         cand_sc[wave * 16 + lane] = mine;
     }
     __syncthreads();
     if (wave != 0) return;
     // the token's top-K among the 4K candidates (one a lane)
-    uint64_t ck = cand_key[lane];
+    uint32_t ck = cand_key[lane];
+    const int ce = cand_e[lane];
     const float cs = cand_sc[lane];
     int my_id = 0;
     mine = 0.0f;
     for (int k = 0; k < K; ++k) {
-        const uint64_t best = wave_max64(ck);
-        const bool hit = ck == best;  // one lane: keys are unique and best is live
-        const int owner = (int)__builtin_ctzll(__ballot(hit));
-        ck = hit ? 0ull : ck;
-        const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), owner));
+        const uint32_t M = wave_max_u32_dpp(ck);
+        const int wl = winner_lane(ck == M, ce);
+        ck = lane == wl ? 0u : ck;
+        const float s_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), wl));
+        const int e_win = __builtin_amdgcn_readlane(ce, wl);
         if (lane == k) {
             mine = s_win;
-            my_id = (int)(~(uint32_t)best);
+            my_id = e_win;
         }
     }
     float sum = 0.0f;
@@ -177,10 +191,11 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
                                               float* __restrict__ weights,
                                               uint8_t* __restrict__ slot_of) {
     wave_priority_high();
-    __shared__ uint64_t cand_key[64];
+    __shared__ uint32_t cand_key[64];
+    __shared__ int cand_e[64];
     __shared__ float cand_sc[64];
     topk_token(blockIdx.x, E, K, src + (size_t)blockIdx.x * E, bias, renorm, scale, ids, weights,
-               slot_of, cand_key, cand_sc);
+               slot_of, cand_key, cand_e, cand_sc);
 }
 
 // The front GEMM's split partials [S][T][N] (router rows [0, E), latent rows [E, E + L))
@@ -201,7 +216,8 @@ __global__ __launch_bounds__(256) void k_front_topk(int T, int N, int E, int L, 
                                                     uint8_t* __restrict__ scales) {
     wave_priority_high();
     __shared__ __attribute__((aligned(16))) float lg[1024];
-    __shared__ uint64_t cand_key[64];
+    __shared__ uint32_t cand_key[64];
+    __shared__ int cand_e[64];
     __shared__ float cand_sc[64];
     if ((int)blockIdx.x < T) {
         const int t = blockIdx.x;
@@ -211,7 +227,8 @@ __global__ __launch_bounds__(256) void k_front_topk(int T, int N, int E, int L, 
             *(v4f*)(logits + (size_t)t * E + c) = v;
         }
         __syncthreads();
-        topk_token(t, E, K, lg, bias, renorm, scale, ids, weights, slot_of, cand_key, cand_sc);
+        topk_token(t, E, K, lg, bias, renorm, scale, ids, weights, slot_of, cand_key, cand_e,
+                   cand_sc);
         return;
     }
     const long b = (long)(blockIdx.x - T) * 256 + threadIdx.x;

@@ -90,6 +90,22 @@ def test_topk_and_lists_shapes(orc, T, E, K, unit):
     check_lists(orc, d, ids)
 
 
+@pytest.mark.parametrize("K", [16, 6])
+def test_topk_exact_ties_across_wavefronts(orc, K):
+    # five logit values and two bias values: many keys s + bias are bit-identical, within a
+    # wavefront, across the four wavefronts and among their winners; equal keys must go
+    # to the lower expert id in every slot
+    T, E = 9, 896
+    g = np.random.default_rng(21 + K)
+    logits = g.integers(-2, 3, size=(T, E)).astype(np.float32)
+    bias = g.choice(np.array([0.0, 0.25], np.float32), size=E)
+    d = moe.dims(T, T, experts=E, top_k=K)
+    ids, w = run_topk(d, logits, bias)
+    rid, rw = orc.topk(logits, bias, K, 1, 2.5)
+    assert np.array_equal(ids, rid)
+    assert np.array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
 def test_topk_saturated_logits(orc):
     # logits far in both tails exercise the sigmoid's boundary rules
     T, E, K = 4, 64, 16

@@ -510,10 +510,13 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
             return false;
         if (launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh) != hipSuccess)
             return false;
-        // the down GEMM's split partials stay in the side scratch: the up-projection's
-        // reduce adds them (shared rounded once to BF16) before it adds its own
+        // the down GEMM's split partials, added on the side stream into the shared
+        // expert's BF16 output (one rounding), which the up-projection's reduce adds to
         if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
                          parts_side, sh, false, &s_sd, kSideShareDown) != hipSuccess)
+            return false;
+        if (launch_wg_reduce(T, H, 0, H, s_sd, parts_side, nullptr, 1, shared, nullptr, sh,
+                             false) != hipSuccess)
             return false;
         return !ss || hipEventRecord(ss->join, sh) == hipSuccess;
     };
@@ -586,7 +589,8 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         MOE_TRY(launch_wgemm(T, H, H, H, L, normed, w->w_up, nullptr, nullptr, dpack, parts, s,
                              false, &s_up, 1.0, nullptr, !late_fork));
         if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
-        MOE_TRY(launch_wg_reduce_combine(T, H, s_up, parts, s_sd, parts_side, shared, out, s));
+        // out = BF16(FP32(shared) + the up-projection's partials in split order)
+        MOE_TRY(launch_wg_reduce(T, H, 0, H, s_up, parts, nullptr, 2, out, shared, s, false));
     } else {
         if (ss) MOE_TRY(hipStreamWaitEvent(s, ss->join, 0));
         MOE_TRY(launch_gemm(T, H, L, normed, w->w_up, out, shared, 2, uni, s));

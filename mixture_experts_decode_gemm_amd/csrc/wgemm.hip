@@ -377,37 +377,6 @@ hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* pa
     return hipGetLastError();
 }
 
-// The up-projection's reduce with the shared expert's down-projection reduce folded in:
-// shared = BF16(the S2 shared partials added in split order), written out, then out =
-// BF16(FP32(shared) + the S up partials added in split order) -- the same two roundings
-// as reducing the shared partials on their own first.  Four columns a thread.
-__global__ __launch_bounds__(256) void k_wg_reduce_combine(int M, int N, int S,
-                                                           const float* __restrict__ part, int S2,
-                                                           const float* __restrict__ part2,
-                                                           uint2* __restrict__ shared,
-                                                           uint2* __restrict__ out) {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)M * (N / 4)) return;
-    const size_t zs = (size_t)M * N;
-    const v4f a = sum_splits(part2 + idx * 4, zs, S2);
-    v4f v = sum_splits(part + idx * 4, zs, S);
-    const uint2 sh = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-    shared[idx] = sh;
-    v[0] += bf16_lo(sh.x);
-    v[1] += bf16_hi(sh.x);
-    v[2] += bf16_lo(sh.y);
-    v[3] += bf16_hi(sh.y);
-    out[idx] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-}
-
-hipError_t launch_wg_reduce_combine(int M, int N, int S, const float* parts, int S2,
-                                    const float* parts2, void* shared, void* out, hipStream_t s) {
-    const long n = (long)M * (N / 4);
-    hipLaunchKernelGGL(k_wg_reduce_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M,
-                       N, S, parts, S2, parts2, (uint2*)shared, (uint2*)out);
-    return hipGetLastError();
-}
-
 // The front GEMM's reduce with the MXFP8 quantisation of the latent folded in: threads
 // below M * N0/4 add four logit columns each (FP32 out); each later thread owns eight
 // columns of one token's latent: it adds their split partials in split order, rounds them

@@ -560,8 +560,7 @@ template <int IS, int MT>
 struct DownStage {
     uint4 w[MT][IS];
     uint32_t sw[MT][IS];  // scale dwords of each row (byte g = K block 4s+g)
-    v8i b[IS];
-    uint32_t bs[IS];      // the hidden's scale dwords
+    uint32_t bs[IS];      // the hidden's scale dwords (the hidden itself goes through LDS)
     int4 un;
     int j, pair;
 };
@@ -595,18 +594,38 @@ __device__ __forceinline__ void down_issue_weights(DownStage<IS, MT>& st, int it
     }
 }
 
-// lanes past the group's last pair load a valid pair's hidden; their output columns are
-// never stored
+// The MXFP8 hidden of a token group, shared by the four wavefronts (each takes all K
+// steps of its own rows): wavefront s brings K step s of the group's tokens into the
+// stage's LDS buffer `hb` (IS x 2 KiB: step s at 2048 s, token r at 128 r, its 16-byte
+// chunk c at position c ^ (r & 7), as in the up projection), eight whole 128-byte rows
+// per direct load, the second eight skipped for groups of at most eight tokens.  Rows past
+// the group's last token hold its last token.  The scale dwords are register loads.
 template <int IS, int MT>
-__device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st,
-                                                const uint8_t* __restrict__ hid,
-                                                const uint8_t* __restrict__ hid_scales) {
+__device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st, int n0,
+                                                const uint8_t* __restrict__ hid, int hbytes,
+                                                const uint8_t* __restrict__ hid_scales,
+                                                uint8_t* hb) {
     constexpr int I = IS * 128, SROW = I / 32;
-    const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-    for (int s = 0; s < IS; ++s) st.b[s] = load_fp8x32(hid + (size_t)st.pair * I + s * 128, g);
+    const int lane = threadIdx.x & 63;
+    // the wavefront index as a scalar: the branch and the LDS base are then uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = lane >> 3, pos = lane & 7;
+    if (wave < IS) {
+        const uint32_t chunk = (uint32_t)(wave * 128 + ((pos ^ q) << 4));
+        const uint32_t p0 = (uint32_t)__shfl(st.pair, q, 64);
+        dma16(hid, hbytes, p0 * I + chunk, (lds_ptr)(hb + wave * 2048));
+        if (st.un.w - n0 > 8) {  // (uniform)
+            const uint32_t p1 = (uint32_t)__shfl(st.pair, 8 + q, 64);
+            dma16(hid, hbytes, p1 * I + chunk, (lds_ptr)(hb + wave * 2048 + 1024));
+        }
+    }
     load_dwords<IS>(hid_scales + (size_t)st.pair * SROW, st.bs);
 }
+
+// VMEM instructions of down_issue_weights (the pair id, MT*IS fragments and MT rows of
+// scale dwords): a compute that follows the next item's weight issue waits with this count
+template <int IS, int MT>
+constexpr int down_weight_loads() { return 1 + MT * IS + MT * (IS / 4 + (IS % 4 ? 1 : 0)); }
 
 // The wavefront's output block is 16 tokens x 16*MT columns of BF16.  It is staged in
 // the wavefront's own LDS area ([token][column], rows padded by 16 bytes) and written
@@ -616,11 +635,28 @@ __device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st,
 template <int MT>
 constexpr int down_stage_row() { return 32 * MT + 16; }
 
-template <int IS, int MT>
-__device__ __forceinline__ void down_mfma_stage(DownStage<IS, MT>& st, uint8_t* stage) {
+// NV: the VMEM instructions issued after the group's hidden (its direct loads are not
+// tracked by the compiler, so each wavefront waits for its own explicitly, then the
+// barrier makes every wavefront's share visible).  cnt: the group's tokens (1..16);
+// column r16 takes token min(r16, cnt - 1), the token whose pair id the lane holds.
+template <int IS, int MT, int NV>
+__device__ __forceinline__ void down_mfma_stage(DownStage<IS, MT>& st, const uint8_t* hb,
+                                                int cnt, uint8_t* stage) {
     constexpr int ROWB = down_stage_row<MT>();
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g = lane >> 4;
+    wait_vmcnt<NV>();
+    lds_sync();  // every wavefront's K step landed (no fragment read moves above it)
+    const int tr = min(r16, cnt - 1), sw = tr & 7;
+    const uint8_t* row = hb + tr * 128;
+    v8i b[IS];
+#pragma unroll
+    for (int s = 0; s < IS; ++s) {
+        const uint4 lo = *(const uint4*)(row + s * 2048 + ((g ^ sw) << 4));
+        const uint4 hi = *(const uint4*)(row + s * 2048 + (((4 + g) ^ sw) << 4));
+        b[s] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
     v4f acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -628,7 +664,7 @@ __device__ __forceinline__ void down_mfma_stage(DownStage<IS, MT>& st, uint8_t* 
     for (int s = 0; s < IS; ++s)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][s]), st.b[s], acc[m],
+            acc[m] = mfma_fp4_fp8(as_fp4_operand(st.w[m][s]), b[s], acc[m],
                                   (int)(st.sw[m][s] >> (8 * g)), (int)(st.bs[s] >> (8 * g)));
     // acc[m][i] = out[token r16][column m*16 + 4g + i]
 #pragma unroll
@@ -662,20 +698,25 @@ __device__ __forceinline__ void down_store(const DownStage<IS, MT>& st, int n0, 
 
 // The item's first token group is computed and left staged (the caller stores it, before
 // the next activation loads); later groups of a hot expert are stored at once.
+// The first group's hidden is followed by the next item's weight issue (and at most the
+// conditional ticket, older).  A later group reuses the buffer once every wavefront is
+// done reading the one before (a barrier ahead of its loads).
 template <int IS, int MT>
 __device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L, bool store,
-                                             const uint8_t* __restrict__ hid,
+                                             const uint8_t* __restrict__ hid, int hbytes,
                                              const uint8_t* __restrict__ hid_scales,
                                              const int32_t* __restrict__ pairs,
-                                             uint16_t* __restrict__ rows, uint8_t* stage) {
+                                             uint16_t* __restrict__ rows, uint8_t* hb,
+                                             uint8_t* stage) {
     const int r16 = threadIdx.x & 15;
-    down_mfma_stage(st, stage);
+    down_mfma_stage<IS, MT, down_weight_loads<IS, MT>()>(st, hb, min(st.un.w, 16), stage);
     if (st.un.w <= 16) return;
     down_store(st, 0, L, store, rows, stage);
     for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later pair groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
-        down_issue_acts(st, hid, hid_scales);
-        down_mfma_stage(st, stage);
+        lds_sync();
+        down_issue_acts(st, n0, hid, hbytes, hid_scales, hb);
+        down_mfma_stage<IS, MT, 0>(st, hb, min(st.un.w - n0, 16), stage);
         down_store(st, n0, L, store, rows, stage);
     }
 }
@@ -686,8 +727,10 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     const uint8_t* __restrict__ hid, const uint8_t* __restrict__ hid_scales,
     const int32_t* __restrict__ pairs, const int4* __restrict__ units,
     const int32_t* __restrict__ num_units, uint16_t* __restrict__ rows,
-    unsigned* __restrict__ counter, int dyn) {
+    unsigned* __restrict__ counter, int dyn, int hbytes) {
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][16 * (32 * MT + 16)];
+    // the hidden of stage A's and stage B's current token group (see down_issue_acts)
+    __shared__ __attribute__((aligned(1024))) uint8_t hbuf[2][IS * 2048];
     __shared__ int tick[2];
     __shared__ int4 un_lds[1024];  // the first D units, as in the up projection
     uint8_t* stage = stage_all[threadIdx.x >> 6];
@@ -705,7 +748,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     int t_prev = 0;
     DownStage<IS, MT> A, B;
     down_issue_weights<IS, MT, PACKED>(A, a, nt, L, w2, s2, pairs, un_lds);
-    down_issue_acts(A, hid, hid_scales);
+    down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0]);
     // items in pairs, nothing conditional between a stage's loads and its compute, each
     // stage's stores right after its compute (see the up projection); the dynamic tail's
     // tickets as there, published through one barrier a stage
@@ -714,7 +757,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         const int t_b = k + 1 < R ? 0 : take_ticket(counter);
         down_issue_weights<IS, MT, PACKED>(B, b_real ? b : a, nt, L, w2, s2, pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        down_compute(A, L, true, hid, hid_scales, pairs, rows, stage);
+        down_compute(A, L, true, hid, hbytes, hid_scales, pairs, rows, hbuf[0], stage);
         int a_next = a + 2 * G;
         if (k + 1 >= R) {  // uniform
             if (threadIdx.x == 0) tick[0] = t_prev;
@@ -723,12 +766,12 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         }
         if (A.un.w <= 16) down_store(A, 0, L, true, rows, stage);
         __builtin_amdgcn_sched_barrier(0);
-        down_issue_acts(B, hid, hid_scales);
+        down_issue_acts(B, 0, hid, hbytes, hid_scales, hbuf[1]);
         t_prev = k + 2 < R ? 0 : take_ticket(counter);
         down_issue_weights<IS, MT, PACKED>(A, a_next < items ? a_next : a, nt, L, w2, s2, pairs,
                                            un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        down_compute(B, L, b_real, hid, hid_scales, pairs, rows, stage);
+        down_compute(B, L, b_real, hid, hbytes, hid_scales, pairs, rows, hbuf[1], stage);
         int b_next = b + 2 * G;
         if (k + 1 >= R) {
             if (threadIdx.x == 0) tick[1] = t_b;
@@ -737,7 +780,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         }
         if (B.un.w <= 16) down_store(B, 0, L, b_real, rows, stage);
         __builtin_amdgcn_sched_barrier(0);
-        down_issue_acts(A, hid, hid_scales);
+        down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0]);
         __builtin_amdgcn_sched_barrier(0);
         if (a_next >= items) break;
         a = a_next;
@@ -830,6 +873,7 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
         hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, counters, 16);
     const int4* un = (const int4*)units;
     const int cbytes = T * L;  // the MXFP8 latent's codes (< 2^31: T <= 4096, L <= 3584)
+    const int hbytes = T * K * I;  // the MXFP8 hidden (< 2^31: T K <= 65536, I <= 512)
     const int up_items = E * (I / UP_COLS);  // an upper bound: the kernels read D on the device
     const int cus = num_cus();
     const dim3 blk(256);
@@ -865,11 +909,11 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
         if (packed && MT == 8)                                                               \
             hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, true>), dgrid, blk, 0, s, L, w2, s2, \
                                hid, hsc, pairs, un, num_units, (uint16_t*)rows,              \
-                               counters + 8, dyn);                                           \
+                               counters + 8, dyn, hbytes);                                   \
         else                                                                                 \
             hipLaunchKernelGGL((k_ffn_down_fast<IS, MT, false>), dgrid, blk, 0, s, L, w2, s2,\
                                hid, hsc, pairs, un, num_units, (uint16_t*)rows,              \
-                               counters + 8, dyn);                                           \
+                               counters + 8, dyn, hbytes);                                   \
         break;
         MOE_DOWN(8, 1) MOE_DOWN(8, 2) MOE_DOWN(8, 4) MOE_DOWN(4, 1) MOE_DOWN(4, 2)
         MOE_DOWN(4, 4)

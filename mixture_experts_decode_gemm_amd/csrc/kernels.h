@@ -101,11 +101,6 @@ hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, cons
 // [N0, N1) to out1 with mode1 0 FP32, 1 BF16, 2 BF16 of add1 + sum; columns past N1 untouched
 hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* parts, float* out0,
                             int mode1, void* out1, const void* add1, hipStream_t s, bool prio);
-// the front GEMM's reduce: logits FP32 (columns [0, N0)) and, for columns [N0, N1), the
-// latent rounded once to BF16 with its MXFP8 codes and scales ((N1 - N0) % 32 == 0)
-hipError_t launch_wg_reduce_front(int M, int N, int N0, int N1, int S, const float* parts,
-                                  float* logits, void* latent, uint8_t* codes, uint8_t* scales,
-                                  hipStream_t s);
 // W [N, K] BF16 -> the packed layout (N % 64 == 0, K % 64 == 0)
 hipError_t launch_pack_dense(int N, int K, const void* w, void* out, hipStream_t s);
 

@@ -377,41 +377,6 @@ hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* pa
     return hipGetLastError();
 }
 
-// The front GEMM's reduce with the MXFP8 quantisation of the latent folded in: threads
-// below M * N0/4 add four logit columns each (FP32 out); each later thread owns eight
-// columns of one token's latent: it adds their split partials in split order, rounds them
-// once to BF16 (the latent, written out), and with the three other threads of its
-// 32-column block (neighbouring lanes: the block's amax by lane shuffles) writes the
-// block's E4M3 codes and E8M0 scale.
-__global__ __launch_bounds__(256) void k_wg_reduce_front(int M, int N, int N0, int N1, int S,
-                                                         const float* __restrict__ part,
-                                                         float* __restrict__ logits,
-                                                         uint4* __restrict__ latent,
-                                                         uint2* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales) {
-    wave_priority_high();
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    const size_t zs = (size_t)M * N;
-    const long nlog = (long)M * (N0 / 4);  // a multiple of 8: blocks of four lanes align
-    if (idx < nlog) {
-        const int m = (int)(idx / (N0 / 4)), c = (int)(idx - (long)m * (N0 / 4)) * 4;
-        *(v4f*)(logits + (size_t)m * N0 + c) = sum_splits(part + (size_t)m * N + c, zs, S);
-        return;
-    }
-    const long b = idx - nlog;
-    if (b >= (long)M * ((N1 - N0) / 8)) return;  // whole blocks of four: (N1 - N0) % 32 == 0
-    front_latent8(b, M, N, N0, N1, S, part, latent, codes, scales);
-}
-
-hipError_t launch_wg_reduce_front(int M, int N, int N0, int N1, int S, const float* parts,
-                                  float* logits, void* latent, uint8_t* codes, uint8_t* scales,
-                                  hipStream_t s) {
-    const long n = (long)M * (N0 / 4) + (long)M * ((N1 - N0) / 8);
-    hipLaunchKernelGGL(k_wg_reduce_front, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M, N,
-                       N0, N1, S, parts, logits, (uint4*)latent, (uint2*)codes, scales);
-    return hipGetLastError();
-}
-
 // ---- packed dense layout ---------------------------------------------------------------
 // W [N, K] BF16 row-major -> blocks of 1 KiB: [N/64 row groups][K/64 K stages][tile 2]
 // [K step 4][lane 64][8 BF16], lane l of (group g, stage s, tile i, step q) holding row

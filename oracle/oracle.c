@@ -236,8 +236,9 @@ void orc_topk(int T, int E, int K, const float* logits, const float* bias, int r
 }
 
 /* [wide] WideRoute (each (token, slot) pair appended to its expert's list, encoded
-   token*16 + slot) and the module summary ("unit windows built from the routing
-   lists: every touched expert streams once per 8 of its tokens").  The pages fill
+   token*16 + slot) and the module summary (the routing lists are cut into windows of 8
+   tokens, and the grouped engine passes over a touched expert's weights once per such
+   window).  The pages fill
    lists with atomic claims, so the order inside a list is theirs to choose; here a
    list holds its pairs in ascending pair id.  A unit is a window of unit_tokens
    consecutive entries of one list: (expert, first list entry, window length, the

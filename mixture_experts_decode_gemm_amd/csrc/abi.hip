@@ -505,19 +505,36 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
             if (hipEventRecord(ss->fork, s) != hipSuccess) return false;
             if (hipStreamWaitEvent(sh, ss->fork, 0) != hipSuccess) return false;
         }
-        if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr, dpack,
-                         parts_side, sh, false, &s_gu, kSideShareGu) != hipSuccess)
-            return false;
-        if (launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh) != hipSuccess)
-            return false;
-        // the down GEMM's split partials, added on the side stream into the shared
-        // expert's BF16 output (one rounding), which the up-projection's reduce adds to
-        if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
-                         parts_side, sh, false, &s_sd, kSideShareDown) != hipSuccess)
-            return false;
-        if (launch_wg_reduce(T, H, 0, H, s_sd, parts_side, nullptr, 1, shared, nullptr, sh,
-                             false) != hipSuccess)
-            return false;
+        if (late_fork) {  // unsplit: the BF16 gate/up values in the side scratch
+            if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr,
+                             dpack, parts_side, sh, false, &s_gu, kSideShareGu, nullptr, false,
+                             parts_side) != hipSuccess)
+                return false;
+            if (launch_silu_mul(T, S, parts_side, act, sh) != hipSuccess) return false;
+        } else {
+            if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr,
+                             dpack, parts_side, sh, false, &s_gu, kSideShareGu) != hipSuccess)
+                return false;
+            if (launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh) != hipSuccess)
+                return false;
+        }
+        // the down GEMM into the shared expert's BF16 output (one rounding), which the
+        // up-projection's reduce adds to: forked late (beside the expert passes, which
+        // leave it time to spare) unsplit and written directly, else as split partials
+        // reduced on the side stream
+        if (late_fork) {
+            if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
+                             parts_side, sh, false, &s_sd, kSideShareDown, nullptr, false,
+                             shared) != hipSuccess)
+                return false;
+        } else {
+            if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
+                             parts_side, sh, false, &s_sd, kSideShareDown) != hipSuccess)
+                return false;
+            if (launch_wg_reduce(T, H, 0, H, s_sd, parts_side, nullptr, 1, shared, nullptr, sh,
+                                 false) != hipSuccess)
+                return false;
+        }
         return !ss || hipEventRecord(ss->join, sh) == hipSuccess;
     };
     // the routing slot map (for the list build past one workgroup), filled by the top-K

@@ -87,6 +87,8 @@ hipError_t launch_silu_mul_parts(int M, int S, int nsplit, const float* parts, i
 // the split count.  wgemm_fits tells whether the shape is supported (K % 128 == 0, every
 // segment a multiple of 32 rows, of 64 when packed, M * K < 2^31).  zero (optional): 16
 // words the launch sets to 0, for the counters of a later launch on the same stream.
+// out_bf16 (optional, N0 = N1 = N): one split, the result rounded once to BF16 and written
+// to out_bf16 [M, N] directly (no partials, no reduce; parts unused).
 bool wgemm_fits(int M, int N, int N0, int N1, int K, bool packed);
 // share: the fraction of the GPU the split plan assumes (1 when the GEMM runs alone);
 // parts_once: the plan counts the partials' bytes once, not written and read back (for a
@@ -96,7 +98,7 @@ size_t wgemm_parts_bytes(int M, int N, int K, double share = 1.0, bool parts_onc
 hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
                         const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
                         bool prio, int* S, double share = 1.0, unsigned* zero = nullptr,
-                        bool parts_once = false);
+                        bool parts_once = false, void* out_bf16 = nullptr);
 // adds the S partials (rows of stride N) in split order: columns [0, N0) to out0 (FP32),
 // [N0, N1) to out1 with mode1 0 FP32, 1 BF16, 2 BF16 of add1 + sum; columns past N1 untouched
 hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* parts, float* out0,

@@ -45,6 +45,7 @@ struct WgArgs {
     const uint16_t* w[3];  // row segments [0, N0), [N0, N1), [N1, N): row-major or packed
     float* part;           // [S][M][N] FP32
     unsigned* zero;        // optional: 16 words workgroup 0 sets to 0 (for a later launch)
+    uint16_t* out;         // optional, with S = 1: BF16 [M, N] written directly, no partials
     int M, K, N, N0, N1, S, NX, MCH, prio;  // M chunks of 32 * MT32 tokens
 };
 
@@ -185,6 +186,20 @@ __global__ __launch_bounds__(512, 1) void k_wgemm(const WgArgs a) {
     wait_vmcnt<0>();  // no direct load may still target LDS when the workgroup ends
     if (n0 >= a.N) return;
     // D layout: lane holds token column r32 of the tile, rows 8 (v / 4) + 4 h + v % 4
+    if (a.out) {  // one split: the sum is final, rounded once to BF16
+#pragma unroll
+        for (int t = 0; t < MT32; ++t) {
+            const int m = m0 + t * 32 + r32;
+            if (m >= a.M) continue;
+            uint16_t* dst = a.out + (size_t)m * a.N + n0 + 4 * h;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *(uint2*)(dst + 8 * jj) =
+                    make_uint2(pack_bf16x2(acc[t][4 * jj], acc[t][4 * jj + 1]),
+                               pack_bf16x2(acc[t][4 * jj + 2], acc[t][4 * jj + 3]));
+        }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < MT32; ++t) {
         const int m = m0 + t * 32 + r32;
@@ -217,7 +232,7 @@ struct WgPlan {
 // steps up to 256, 128-token steps past it) with one plan each.
 static int wg_class(int M) { return M <= 256 ? (M + 31) / 32 * 32 : (M + 127) / 128 * 128; }
 
-static WgPlan wg_plan(int M, int N, int K, double share, bool parts_once) {
+static WgPlan wg_plan(int M, int N, int K, double share, bool parts_once, int smax = 64) {
     const int KS = 64;  // (128-deep stages measured no faster at the layer's shapes)
     const int NX = (N + 255) / 256;
     const int Q = K / (2 * KS);
@@ -235,7 +250,7 @@ static WgPlan wg_plan(int M, int N, int K, double share, bool parts_once) {
         if (chunk == 128 && M <= 128) break;
         const int mch = (M + chunk - 1) / chunk;
         const int mt32 = M < chunk ? (M + 31) / 32 : chunk / 32;
-        for (int S = 1; S <= Q && S <= 64; ++S) {
+        for (int S = 1; S <= Q && S <= smax; ++S) {
             const double wgs = (double)NX * mch * S;
             const double rounds = (double)(long)((wgs + cus - 1) / cus);
             const double kz = (double)((Q + S - 1) / S) * 2 * KS;  // the longest K range
@@ -302,10 +317,12 @@ static hipError_t launch_ks(const WgArgs& a, int mt32, bool packed, int G, hipSt
 
 hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, const void* w0,
                         const void* w1, const void* w2, bool packed, float* parts, hipStream_t s,
-                        bool prio, int* S, double share, unsigned* zero, bool parts_once) {
-    const WgPlan p = wg_plan(M, N, K, share, parts_once);
+                        bool prio, int* S, double share, unsigned* zero, bool parts_once,
+                        void* out_bf16) {
+    const WgPlan p = wg_plan(M, N, K, share, parts_once, out_bf16 ? 1 : 64);
     WgArgs a;
     a.zero = zero;
+    a.out = (uint16_t*)out_bf16;
     a.x = (const uint16_t*)x;
     a.w[0] = (const uint16_t*)w0;
     a.w[1] = (const uint16_t*)(w1 ? w1 : w0);

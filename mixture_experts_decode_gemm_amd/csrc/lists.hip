@@ -154,34 +154,29 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
 
 // Exclusive prefix sums of three values at once over a 1024-thread block (one pass:
 // wave scans by shuffles, the 16 wave totals scanned by one wavefront); totals returned.
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (no LDS round
+// trips): shifts by 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted in from
+// outside the row read 0), then the last lane of row 0 added into row 1 and of row 2 into
+// row 3 (row broadcast 15), then the last lane of row 1 into rows 2 and 3 (row broadcast
+// 31).  Lanes a masked row does not write read the old value, 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+    return x;
+}
+
 __device__ int3 block_exclusive_scan3_1024(int3 v, int3* smem, int3* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int3 x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int a = __shfl_up(x.x, off, 64), b = __shfl_up(x.y, off, 64),
-                  c = __shfl_up(x.z, off, 64);
-        if (lane >= off) {
-            x.x += a;
-            x.y += b;
-            x.z += c;
-        }
-    }
+    const int3 x = make_int3(wave_incl_scan(v.x), wave_incl_scan(v.y), wave_incl_scan(v.z));
     if (lane == 63) smem[wave] = x;
     __syncthreads();
     if (wave == 0) {
-        int3 w = lane < 16 ? smem[lane] : make_int3(0, 0, 0);
-        int3 y = w;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const int a = __shfl_up(y.x, off, 64), b = __shfl_up(y.y, off, 64),
-                      c = __shfl_up(y.z, off, 64);
-            if (lane >= off) {
-                y.x += a;
-                y.y += b;
-                y.z += c;
-            }
-        }
+        const int3 w = lane < 16 ? smem[lane] : make_int3(0, 0, 0);
+        const int3 y = make_int3(wave_incl_scan(w.x), wave_incl_scan(w.y), wave_incl_scan(w.z));
         if (lane < 16) smem[lane] = make_int3(y.x - w.x, y.y - w.y, y.z - w.z);
         if (lane == 15) smem[16] = y;
     }
@@ -212,11 +207,10 @@ __device__ __forceinline__ void load_token_ids(const int32_t* __restrict__ ids, 
 
 // The whole build in one workgroup when the bitmaps fit in LDS (decode batches up to a
 // few hundred tokens): the three steps above with the bitmaps and list offsets in LDS and
-// block barriers between them, and a scatter fill -- the thread of token t places each of
-// its pairs (t, k) at offsets[e] + (the tokens before t that chose e: set bits of e's
-// bitmap below t).  A slot repeating an earlier slot's id is dropped, as in the marking.
-// Thread i owns tokens i, i + 1024, ...; the ids of its first token stay in registers
-// between the marking and the fill.
+// block barriers between them, and a scatter fill -- a token's pair (t, k) goes to
+// offsets[e] + (the tokens before t that chose e: set bits of e's bitmap below t).  A slot
+// repeating an earlier slot's id is dropped, as in the marking.  Four threads share a
+// token, each taking four of its slots.
 // LDS of the one-workgroup build: bitmaps [W][E] u32, list offsets [E] u32, and -- when
 // the whole stays within kListsLds -- the per-word list positions [W][E] u16
 constexpr size_t kListsLds = 61440;
@@ -248,20 +242,32 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
     // pre[w][e] = offsets[e] + the set bits of e's words below w (< 2^16: T*K <= 65536)
     uint16_t* pre = (uint16_t*)(offl + E);   // [W][E]
     const bool use_pre = lists_prefix_fits(T, E);
-    const int t0 = threadIdx.x;
+    // four threads a token (tokens t0, t0 + 256, ...), thread q of a token taking its slots
+    // 4 q .. 4 q + 3; the ids of the first token stay in registers from the marking to the
+    // fill
+    const int q = threadIdx.x & 3, t0 = threadIdx.x >> 2;
     int32_t v0[16];
     if (t0 < T) load_token_ids(ids, t0, K, v0);
     for (int i = threadIdx.x; i < W * E; i += 1024) bm[i] = 0;
     __syncthreads();
+    // slot 4 q + j of a token's ids (a select chain: no dynamically indexed registers)
+    auto slot_id = [&](const int32_t v[16], int j) {
+        int ek = -1;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) ek = kk == 4 * q + j ? v[kk] : ek;
+        return ek;
+    };
     auto mark = [&](int t, const int32_t v[16]) {
         const uint32_t bit = 1u << (t & 31);
         uint32_t* row = bm + (t >> 5) * E;
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-            if (k < K && v[k] >= 0 && v[k] < E) atomicOr(&row[v[k]], bit);
+        for (int j = 0; j < 4; ++j) {
+            const int ek = slot_id(v, j);
+            if (4 * q + j < K && ek >= 0 && ek < E) atomicOr(&row[ek], bit);
+        }
     };
     if (t0 < T) mark(t0, v0);
-    for (int t = t0 + 1024; t < T; t += 1024) {
+    for (int t = t0 + 256; t < T; t += 256) {
         int32_t v[16];
         load_token_ids(ids, t, K, v);
         mark(t, v);
@@ -303,15 +309,18 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
         num_units[3] = 0;
     }
     __syncthreads();  // offl complete
+    // the fill, in the marking's layout (the repeat check looks at every earlier slot of
+    // the token): all the workgroup's threads take part and each one's LDS reads go out
+    // together
     auto fill = [&](int t, const int32_t v[16]) {
         const int w = t >> 5;
         const uint32_t below = (1u << (t & 31)) - 1u;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int ek = v[k];
+        for (int j = 0; j < 4; ++j) {
+            const int k = 4 * q + j, ek = slot_id(v, j);
             bool first = k < K && ek >= 0 && ek < E;
 #pragma unroll
-            for (int k2 = 0; k2 < k; ++k2) first = first && v[k2] != ek;
+            for (int k2 = 0; k2 < 15; ++k2) first = first && !(k2 < k && v[k2] == ek);
             if (!first) continue;
             int pos = __popc(bm[w * E + ek] & below);
             if (use_pre) {
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(1024) void k_lists_fused(int T, int K, int E, int u
         }
     };
     if (t0 < T) fill(t0, v0);
-    for (int t = t0 + 1024; t < T; t += 1024) {
+    for (int t = t0 + 256; t < T; t += 256) {
         int32_t v[16];
         load_token_ids(ids, t, K, v);
         fill(t, v);

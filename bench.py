@@ -362,7 +362,14 @@ def main():
                            "achieved": layer_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": layer_gbs / HBM_PEAK_GBS,
                            "phase_bound_us": phase_bound_us(T, D),
-                           "phase_frac": phase_bound_us(T, D) / (ms * 1e3)},
+                           "phase_frac": phase_bound_us(T, D) / (ms * 1e3),
+                           # the pages' unit-window streaming (each touched expert once per
+                           # window of up to 8 of its tokens): reported, not the denominator
+                           "nominal_unit_window_bytes": DENSE_BYTES + nu * EXPERT_BYTES,
+                           "nominal_unit_window_gbs": (DENSE_BYTES + nu * EXPERT_BYTES) / (ms * 1e-3) / 1e9,
+                           # activations the step must move, kept out of the denominator
+                           "activation_bytes": activation_bytes(T),
+                           "activation_gbs": activation_bytes(T) / (ms * 1e-3) / 1e9},
         "roofline": {"kernel": "k_ffn_up_fast (gate/up pass of the grouped expert FFN, "
                                + ("row-major" if a.row_major else "packed") + " expert weights)",
                      "bound": "hbm", "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -401,6 +408,9 @@ def main():
         res["router_front"] = bench_router_front(torch, moe, syn, stream, time_calls, a.steps, dev)
         print(f"# router front {res['router_front']}", file=sys.stderr, flush=True)
         res["copy_probe"] = bench_copy(torch, stream, time_calls)
+        ach = res["copy_probe"]["gbs_read_plus_write"]
+        res["layer_roofline"]["achievable_gbs"] = ach
+        res["layer_roofline"]["frac_of_achievable"] = layer_gbs / ach
     clocks.stop()
 
     if not a.no_cpu_baseline:
@@ -505,6 +515,18 @@ def bench_router_front(torch, moe, syn, stream, time_calls, steps, dev):
                      "touched_experts": int(torch.count_nonzero(counts).item()),
                      "units": int(nu[0].item())}
     return res
+
+
+def activation_bytes(t, h=7168, l=3584, k=16, i=512, s=6144, e=896):
+    """Activation bytes one step must move (split partials excluded: an artefact of the
+    kernels): x read by the front and the shared gate/up GEMMs; FP32 logits written; the
+    latent written in BF16 and MXFP8 and its codes read; the MXFP8 hidden written and read;
+    the BF16 expert rows written and read; the routed and normed latent written and the
+    normed one read; the shared activation written and read; the shared output written and
+    read; the output written."""
+    mx = lambda n: n * 33 // 32  # E4M3 codes + one E8M0 scale per 32
+    return (2 * t * h * 2 + t * e * 4 + t * l * 2 + 2 * mx(t * l) + 2 * mx(t * k * i)
+            + 2 * t * k * l * 2 + 3 * t * l * 2 + 2 * t * s * 2 + 2 * t * h * 2 + t * h * 2)
 
 
 def bench_copy(torch, stream, time_calls):

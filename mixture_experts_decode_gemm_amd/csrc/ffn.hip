@@ -233,21 +233,23 @@ template <int SPW>
 __device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int K, int n0,
                                               const uint8_t* __restrict__ codes, int cbytes,
                                               const uint8_t* __restrict__ scales,
-                                              uint8_t* act) {
+                                              uint8_t* act, bool dma = true) {
     constexpr int L = SPW * 512, SROW = L / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 3, pos = lane & 7;
-    // lane r (< 16) holds the pair of the group's token r
-    const uint32_t t0 = (uint32_t)(__shfl(st.pair, q, 64) / K);
-    const uint32_t t1 = (uint32_t)(__shfl(st.pair, 8 + q, 64) / K);
-    const uint32_t chunk = (uint32_t)((SPW * wave) * 128 + ((pos ^ q) << 4));
-#pragma unroll
-    for (int i = 0; i < SPW; ++i)
-        dma16(codes, cbytes, t0 * L + chunk + i * 128, (lds_ptr)(act + i * 2048));
-    if (st.un.w - n0 > 8) {  // (uniform)
+    if (dma) {  // (uniform) else the area already holds this group
+        // lane r (< 16) holds the pair of the group's token r
+        const uint32_t t0 = (uint32_t)(__shfl(st.pair, q, 64) / K);
+        const uint32_t t1 = (uint32_t)(__shfl(st.pair, 8 + q, 64) / K);
+        const uint32_t chunk = (uint32_t)((SPW * wave) * 128 + ((pos ^ q) << 4));
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
-            dma16(codes, cbytes, t1 * L + chunk + i * 128, (lds_ptr)(act + i * 2048 + 1024));
+            dma16(codes, cbytes, t0 * L + chunk + i * 128, (lds_ptr)(act + i * 2048));
+        if (st.un.w - n0 > 8) {  // (uniform)
+#pragma unroll
+            for (int i = 0; i < SPW; ++i)
+                dma16(codes, cbytes, t1 * L + chunk + i * 128, (lds_ptr)(act + i * 2048 + 1024));
+        }
     }
     const int t = st.pair / K;
     load_dwords<SPW>(scales + (size_t)t * SROW + 4 * SPW * wave, st.bs);
@@ -456,10 +458,23 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int b = a + G;        // the item in stage B
     // dyn = 0: every pass static (no counter is touched)
     const int R = dyn ? static_passes(items, G) : 0x7fffffff, base = dyn ? 2 * R * G : 0;
+    // Within the whole static blocks of 2G items, the two stages of a pass take two
+    // neighbouring column tiles of one expert (a pass still covers one compact window of
+    // 2G items): for an expert of at most 16 tokens stage B then finds the group's
+    // activations already in LDS and loads none.  (Four tiles over two passes would skip
+    // more loads, but hand a hot expert's heavy tiles to one workgroup four at a time:
+    // measured slower with skewed routing.)  Items past those blocks (the dynamic tail, a
+    // last partial block) keep their own order.
+    const int full = min(items, dyn ? 2 * R * G : items) / (2 * G) * (2 * G);
+    auto item_of = [&](int i) {
+        if (i >= full) return i;
+        const int k = i / (2 * G), r = i - k * 2 * G;  // pass, place in it
+        return 2 * (G * k + (r < G ? r : r - G)) + (r < G ? 0 : 1);
+    };
     int t_prev = 0;       // the ticket naming the next A (taken last pass, if dynamic)
     int rb = 0;
     UpStage<SPW> A, B;
-    up_issue_weights<SPW, PACKED>(A, a, nt, I, w13, s13, pairs, un_lds);
+    up_issue_weights<SPW, PACKED>(A, item_of(a), nt, I, w13, s13, pairs, un_lds);
     up_issue_acts(A, K, 0, codes, cbytes, scales, act);
     // Items in pairs (stages A and B), pass k holding a_k and b_k.  Nothing between a
     // stage's loads and its compute is conditional: a conditional exit there would let the
@@ -477,23 +492,26 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
         int* const tk = k + 1 < R ? nullptr : tick;
         // (the scheduling barriers keep each stage's loads ahead of the other stage's
         // compute; otherwise the scheduler interleaves them into it)
-        up_issue_weights<SPW, PACKED>(B, b_real ? b : a, nt, I, w13, s13, pairs, un_lds);
+        up_issue_weights<SPW, PACKED>(B, item_of(b_real ? b : a), nt, I, w13, s13, pairs,
+                                      un_lds);
         __builtin_amdgcn_sched_barrier(0);
         const UpOut oa = up_compute(A, K, I, true, codes, cbytes, scales, pairs, hid, hid_scales,
                                     red, rb, act, tk, t_prev);
         const int a_next = k + 1 < R ? a + 2 * G : ticket_item(base, oa.ticket);
         up_store(oa, hid, hid_scales);
         __builtin_amdgcn_sched_barrier(0);
-        up_issue_acts(B, K, 0, codes, cbytes, scales, act);
+        // (B of A's expert, at most 16 tokens: its one group is still in the area)
+        up_issue_acts(B, K, 0, codes, cbytes, scales, act, !(B.un.x == A.un.x && A.un.w <= 16));
         t_prev = k + 2 < R ? 0 : take_ticket(counter);  // names a_{k+2} if dynamic
-        up_issue_weights<SPW, PACKED>(A, a_next < items ? a_next : a, nt, I, w13, s13, pairs,
-                                      un_lds);
+        const int e_b = B.un.x;
+        up_issue_weights<SPW, PACKED>(A, item_of(a_next < items ? a_next : a), nt, I, w13, s13,
+                                      pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
         const UpOut ob = up_compute(B, K, I, b_real, codes, cbytes, scales, pairs, hid,
                                     hid_scales, red, rb, act, tk, t_b);
         up_store(ob, hid, hid_scales);
         __builtin_amdgcn_sched_barrier(0);
-        up_issue_acts(A, K, 0, codes, cbytes, scales, act);
+        up_issue_acts(A, K, 0, codes, cbytes, scales, act, !(A.un.x == e_b && A.un.w <= 16));
         __builtin_amdgcn_sched_barrier(0);
         if (a_next >= items) break;  // (every later item is larger)
         b = k + 1 < R ? b + 2 * G : ticket_item(base, ob.ticket);

@@ -137,6 +137,9 @@ class Clocks:
             self._t.join()
             self._t = None
 
+    def count(self, t0, t1):
+        return sum(1 for smp in self.samples if t0 <= smp[0] <= t1)
+
     def summary(self, t0, t1):
         if self.mod is None:
             return {"source": "amdsmi", "error": self.err}
@@ -243,6 +246,7 @@ def main():
 
         def step():
             moe.moe_layer(d, lwt, xin, out, ws, stream)
+        hw = time.perf_counter()
         n_warm = warm(step, warmup, floor_s)
         # the K timed steps back to back, one event before and one after them
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -272,7 +276,7 @@ def main():
         return dict(ms=ms, ms_median=statistics.median(per), ms_min=min(per), ms_ev=ms_ev,
                     D=D, units=nu,
                     d=d, v=v, warm_steps=n_warm, host_us=(h1 - h0) / steps * 1e6,
-                    window=(h0, h2))
+                    window=(h0, h2), warm_window=(hw, h2))
 
     def phase_bound_us(t, D):
         """The phase-wise speed of light: the dense projections at max(weight bytes / HBM,
@@ -284,7 +288,14 @@ def main():
 
     clocks.start()
     r = run_T(T, a.steps, a.warmup, WARM_FLOOR_S)
-    clk = clocks.summary(*r["window"])
+    # the clocks over the last 0.1 s of the same work up to the end of the timed steps (the
+    # end of the warm-up included: a short timed run alone holds too few of the firmware's
+    # samples to go by; the start of the warm-up, where the clocks still ramp, left out)
+    h0, h2 = r["window"]
+    t0 = max(r["warm_window"][0], min(h0, h2 - 0.1))
+    clk = clocks.summary(t0, h2)
+    clk["window_s"] = round(h2 - t0, 3)
+    clk["samples_in_timed_steps"] = clocks.count(h0, h2)
     ms, D, nu, d, v = r["ms"], r["D"], r["units"], r["d"], r["v"]
     layer_bytes = DENSE_BYTES + D * EXPERT_BYTES
     layer_gbs = layer_bytes / (ms * 1e-3) / 1e9

@@ -296,6 +296,11 @@ def main():
     clk = clocks.summary(t0, h2)
     clk["window_s"] = round(h2 - t0, 3)
     clk["samples_in_timed_steps"] = clocks.count(h0, h2)
+    # the firmware's table at times returns idle values while the GPU runs at full load
+    # (seen: every sample of a loaded window at ~150-250 MHz): flagged, not corrected
+    med = (clk.get("sclk_xcd_max_mhz") or {}).get("median")
+    if med is not None:
+        clk["plausible"] = med >= 1000
     ms, D, nu, d, v = r["ms"], r["D"], r["units"], r["d"], r["v"]
     layer_bytes = DENSE_BYTES + D * EXPERT_BYTES
     layer_gbs = layer_bytes / (ms * 1e-3) / 1e9

@@ -23,6 +23,11 @@ constexpr int kMaxTopK = 16;
 // 0.3 .. 1; 547 -> 521 us per layer)
 constexpr double kSideShareGu = 0.5;
 constexpr double kSideShareDown = 0.5;
+// up to this many tokens the routed path is short and the shared expert's chain weighs
+// more: its GEMMs are planned for the whole GPU (measured per layer: -15 us at 8 tokens,
+// -24 at 64, -27 at 96, -3.6 at 130; +3.5 at 1 token, +6 at 192 and +8 at 256)
+constexpr int kNarrowSideTokens = 160;
+inline double side_share(int T, double share) { return T <= kNarrowSideTokens ? 1.0 : share; }
 // the front GEMM (router + latent down rows) runs beside the side stream's gate/up GEMM:
 // planned for three quarters of the GPU it takes 4 splits of 128-token chunks, not 5
 // (measured 495.7 -> 487.2 us per layer at 256 tokens)
@@ -99,8 +104,11 @@ Layout layout(const moe_dims* d) {
     lo.uni_side = at;
     size_t us = 0;
     const size_t g2[4] = {gemm_parts_bytes(Tm, S2, Hi), gemm_scratch_bytes(Tm, Hi, d->shared_inter),
-                          wgemm_parts_bytes(Tm, S2, Hi, kSideShareGu),
-                          wgemm_parts_bytes(Tm, Hi, d->shared_inter, kSideShareDown)};
+                          std::max(wgemm_parts_bytes(Tm, S2, Hi, kSideShareGu),
+                                   wgemm_parts_bytes(std::min(Tm, kNarrowSideTokens), S2, Hi, 1.0)),
+                          std::max(wgemm_parts_bytes(Tm, Hi, d->shared_inter, kSideShareDown),
+                                   wgemm_parts_bytes(std::min(Tm, kNarrowSideTokens), Hi,
+                                                     d->shared_inter, 1.0))};
     for (size_t v : g2) us = v > us ? v : us;
     at += up256(us);
     lo.parts = at;
@@ -507,13 +515,13 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         }
         if (late_fork) {  // unsplit: the BF16 gate/up values in the side scratch
             if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr,
-                             dpack, parts_side, sh, false, &s_gu, kSideShareGu, nullptr, false,
+                             dpack, parts_side, sh, false, &s_gu, side_share(T, kSideShareGu), nullptr, false,
                              parts_side) != hipSuccess)
                 return false;
             if (launch_silu_mul(T, S, parts_side, act, sh) != hipSuccess) return false;
         } else {
             if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr,
-                             dpack, parts_side, sh, false, &s_gu, kSideShareGu) != hipSuccess)
+                             dpack, parts_side, sh, false, &s_gu, side_share(T, kSideShareGu)) != hipSuccess)
                 return false;
             if (launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh) != hipSuccess)
                 return false;
@@ -524,12 +532,12 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         // reduced on the side stream
         if (late_fork) {
             if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_sd, kSideShareDown, nullptr, false,
+                             parts_side, sh, false, &s_sd, side_share(T, kSideShareDown), nullptr, false,
                              shared) != hipSuccess)
                 return false;
         } else {
             if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_sd, kSideShareDown) != hipSuccess)
+                             parts_side, sh, false, &s_sd, side_share(T, kSideShareDown)) != hipSuccess)
                 return false;
             if (launch_wg_reduce(T, H, 0, H, s_sd, parts_side, nullptr, 1, shared, nullptr, sh,
                                  false) != hipSuccess)

@@ -515,13 +515,14 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         }
         if (late_fork) {  // unsplit: the BF16 gate/up values in the side scratch
             if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr,
-                             dpack, parts_side, sh, false, &s_gu, side_share(T, kSideShareGu), nullptr, false,
+                             dpack, parts_side, sh, false, &s_gu, kSideShareGu, nullptr, false,
                              parts_side) != hipSuccess)
                 return false;
             if (launch_silu_mul(T, S, parts_side, act, sh) != hipSuccess) return false;
         } else {
             if (launch_wgemm(T, 2 * S, 2 * S, 2 * S, H, x, w->w_shared_gu, nullptr, nullptr,
-                             dpack, parts_side, sh, false, &s_gu, side_share(T, kSideShareGu)) != hipSuccess)
+                             dpack, parts_side, sh, false, &s_gu,
+                             side_share(T, kSideShareGu)) != hipSuccess)
                 return false;
             if (launch_silu_mul_parts(T, S, s_gu, parts_side, 2 * S, act, sh) != hipSuccess)
                 return false;
@@ -532,12 +533,13 @@ moe_status moe_layer(const moe_dims* d, const moe_layer_weights* w, const void* 
         // reduced on the side stream
         if (late_fork) {
             if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_sd, side_share(T, kSideShareDown), nullptr, false,
+                             parts_side, sh, false, &s_sd, kSideShareDown, nullptr, false,
                              shared) != hipSuccess)
                 return false;
         } else {
             if (launch_wgemm(T, H, H, H, S, act, w->w_shared_down, nullptr, nullptr, dpack,
-                             parts_side, sh, false, &s_sd, side_share(T, kSideShareDown)) != hipSuccess)
+                             parts_side, sh, false, &s_sd,
+                             side_share(T, kSideShareDown)) != hipSuccess)
                 return false;
             if (launch_wg_reduce(T, H, 0, H, s_sd, parts_side, nullptr, 1, shared, nullptr, sh,
                                  false) != hipSuccess)

@@ -49,33 +49,24 @@ __global__ __launch_bounds__(256) void k_lists_mark(int T, int K, int E,
     for (int e = threadIdx.x; e < E; e += 256) bm[(size_t)w * E + e] = words[e];
 }
 
-// exclusive prefix sum over a 1024-thread block; returns the total through *total
-__device__ int block_exclusive_scan_1024(int v, int* smem, int* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
+__device__ int3 block_exclusive_scan3_1024(int3 v, int3* smem, int3* total);
+
+// popcounts of expert e's bitmap words w0 .. w0 + 15 (0 past W), their loads issued together
+// (unconditionally, past W from the last word: a load under a branch would be waited for
+// on its own)
+__device__ __forceinline__ void word_popcounts(const uint32_t* __restrict__ bm, int W, int E,
+                                               int e, int w0, int (&pc)[16]) {
+    uint32_t b[16];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) smem[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int i = 0; i < 16; ++i) {
-            const int c = smem[i];
-            smem[i] = run;
-            run += c;
-        }
-        smem[16] = run;
-    }
-    __syncthreads();
-    const int res = smem[wave] + x - v;
-    *total = smem[16];
-    __syncthreads();
-    return res;
+    for (int i = 0; i < 16; ++i) b[i] = bm[(size_t)min(w0 + i, W - 1) * E + e];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pc[i] = w0 + i < W ? __popc(b[i]) : 0;
 }
 
+// One thread per expert: its count (the words' popcounts, sixteen loads in flight; the
+// first 32 kept in registers), one three-value block scan (list offsets, first windows,
+// later windows), then each word's list position (words past 32 loaded again, from L2 by
+// then) and the units.
 __global__ __launch_bounds__(1024) void k_lists_scan(int T, int K, int E, int unit,
                                                      const uint32_t* __restrict__ bm,
                                                      int32_t* __restrict__ wordoff,
@@ -84,25 +75,48 @@ __global__ __launch_bounds__(1024) void k_lists_scan(int T, int K, int E, int un
                                                      int4* __restrict__ units,
                                                      int32_t* __restrict__ num_units) {
     wave_priority_high();
-    __shared__ int smem[17];
+    __shared__ int3 smem[17];
     const int W = (T + 31) / 32;
     const int e = threadIdx.x;
     int c = 0;
-    if (e < E)
-        for (int w = 0; w < W; ++w) {
-            wordoff[(size_t)w * E + e] = c;
-            c += __popc(bm[(size_t)w * E + e]);
+    int pa[16] = {}, pb[16] = {};  // the first 32 words' popcounts, kept for the offsets
+    if (e < E) {
+        word_popcounts(bm, W, E, e, 0, pa);
+        word_popcounts(bm, W, E, e, 16, pb);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c += pa[i] + pb[i];
+        for (int w0 = 32; w0 < W; w0 += 16) {
+            int pc[16];
+            word_popcounts(bm, W, E, e, w0, pc);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c += pc[i];
         }
-    int total_pairs, touched, later_total;
-    const int off = block_exclusive_scan_1024(c, smem, &total_pairs);
+    }
     const int nu = (c + unit - 1) / unit;
     // the first window of every touched expert, then every later window
-    const int fi = block_exclusive_scan_1024(c > 0 ? 1 : 0, smem, &touched);
-    const int li = block_exclusive_scan_1024(nu > 1 ? nu - 1 : 0, smem, &later_total);
+    int3 tot;
+    const int3 ex = block_exclusive_scan3_1024(make_int3(c, c > 0 ? 1 : 0, nu > 1 ? nu - 1 : 0),
+                                               smem, &tot);
+    const int off = ex.x, fi = ex.y, li = ex.z;
+    const int total_pairs = tot.x, touched = tot.y, later_total = tot.z;
     if (e < E) {
+        int run = off;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (i < W) wordoff[(size_t)i * E + e] = run;
+            run += i < 16 ? pa[i] : pb[i - 16];
+        }
+        for (int w0 = 32; w0 < W; w0 += 16) {
+            int pc[16];
+            word_popcounts(bm, W, E, e, w0, pc);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (w0 + i < W) wordoff[(size_t)(w0 + i) * E + e] = run;
+                run += pc[i];
+            }
+        }
         counts[e] = c;
         offsets[e] = off;
-        for (int w = 0; w < W; ++w) wordoff[(size_t)w * E + e] += off;
         if (c > 0) units[fi] = make_int4(e, off, c < unit ? c : unit, c);
         for (int j = 1; j < nu; ++j) {
             const int rest = c - j * unit;
@@ -144,7 +158,9 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
         const int32_t* row = ids + (size_t)t * K;
         int32_t v[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = k < K ? row[k] : -1;
+        for (int k = 0; k < 16; ++k) v[k] = row[min(k, K - 1)];  // (unconditional loads)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = k < K ? v[k] : -1;
         int kk = 0;
 #pragma unroll
         for (int k = 15; k >= 0; --k) kk = v[k] == e ? k : kk;
@@ -152,8 +168,6 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
     }
 }
 
-// Exclusive prefix sums of three values at once over a 1024-thread block (one pass:
-// wave scans by shuffles, the 16 wave totals scanned by one wavefront); totals returned.
 // Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (no LDS round
 // trips): shifts by 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted in from
 // outside the row read 0), then the last lane of row 0 added into row 1 and of row 2 into
@@ -169,6 +183,8 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
+// Exclusive prefix sums of three values at once over a 1024-thread block (one pass: wave
+// scans by DPP moves, the 16 wave totals scanned by one wavefront); totals returned.
 __device__ int3 block_exclusive_scan3_1024(int3 v, int3* smem, int3* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int3 x = make_int3(wave_incl_scan(v.x), wave_incl_scan(v.y), wave_incl_scan(v.z));
@@ -201,7 +217,9 @@ __device__ __forceinline__ void load_token_ids(const int32_t* __restrict__ ids, 
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = k < K ? row[k] : -1;
+        for (int k = 0; k < 16; ++k) v[k] = row[min(k, K - 1)];  // (unconditional loads)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = k < K ? v[k] : -1;
     }
 }
 

@@ -170,30 +170,34 @@ struct UpStage {
     uint4 w[4][SPW];        // FP4 weight fragments
     uint32_t ws[4][SPW];    // their scale dwords (byte g = K block 4s+g)
     uint32_t bs[SPW];       // the activations' scale dwords
-    int4 un;                // (expert, list begin, window, list length)
-    int j, pair;
+    uint32_t bs1[SPW];      // those of the second token group (tokens 16..31)
+    int4 un;                // (expert, list begin, -, list length)
+    int j, pair, pair1;     // pair ids of tokens r and 16 + r of the expert's list
 };
 
 // Every load below is issued unconditionally (indices are clamped, unused lanes load a
 // valid address and discard it) so that the same number of loads is outstanding on every
 // path: the compiler can then wait for exactly the current item's data (s_waitcnt
 // vmcnt(N)) and leave the next item's loads in flight.
-template <int SPW, bool PACKED>
+// un3: the first D units as (expert, list begin, list length) in LDS; DUAL: the second
+// token group's pair ids too (the two-area build, see up_issue_acts)
+template <int SPW, bool PACKED, bool DUAL>
 __device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int nt, int I,
                                                  const uint8_t* __restrict__ w13,
                                                  const uint8_t* __restrict__ s13,
                                                  const int32_t* __restrict__ pairs,
-                                                 const int4* __restrict__ units) {
+                                                 const int* un3) {
     constexpr int L = SPW * 512, SROW = L / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int u = item / nt;
     st.j = item - u * nt;
-    st.un = units[u];
+    st.un = make_int4(un3[3 * u], un3[3 * u + 1], 0, un3[3 * u + 2]);
     const int e = st.un.x;
-    // the first token group's pair ids, issued before the weights so that the
+    // the first two token groups' pair ids, issued before the weights so that the
     // activation addresses can wait on them without waiting on the weights
     st.pair = pairs[st.un.y + min(r16, st.un.w - 1)];
+    if (DUAL) st.pair1 = pairs[st.un.y + min(16 + r16, st.un.w - 1)];
     if (PACKED) {
         // packed layout: this wavefront's fragments are 4*SPW consecutive 1 KiB blocks
         // (tile-major, then step), each in lane order; the scale dwords of tile m, row r16
@@ -229,19 +233,48 @@ __device__ __forceinline__ void up_issue_weights(UpStage<SPW>& st, int item, int
 // eight tokens are skipped when the group has at most eight.  A lane past the group's last
 // token holds a copy of a valid token: MFMA output column n depends on B column n only,
 // and such columns are never stored.  The scale dwords are register loads, issued last.
-template <int SPW>
+//
+// act1 (the first group's call only): an expert of more than 16 tokens also gets its
+// second group's activations, into the wavefront's second area act1, and their scale
+// dwords (bs1) -- issued BEFORE the first group's loads.  Loads complete in issue order,
+// so the first group's exact wait covers the second group's loads as well, and the second
+// group is computed without a wait of its own: the next item's weights stay in flight.
+template <int SPW, bool DUAL>
 __device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int K, int n0,
                                               const uint8_t* __restrict__ codes, int cbytes,
                                               const uint8_t* __restrict__ scales,
-                                              uint8_t* act, bool dma = true) {
+                                              uint8_t* act, bool dma = true,
+                                              uint8_t* act1 = nullptr) {
     constexpr int L = SPW * 512, SROW = L / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 3, pos = lane & 7;
+    // every address first (lane r < 16 holds the pair of the group's token r): the one
+    // wait for the pair ids then comes before any branch, the same on every path (a wait
+    // placed after a branch covers the path that skipped it and here would also wait for
+    // part of the next item's weights)
+    const uint32_t t0 = (uint32_t)(__shfl(st.pair, q, 64) / K);
+    const uint32_t t1 = (uint32_t)(__shfl(st.pair, 8 + q, 64) / K);
+    const int pr1 = DUAL ? st.pair1 : 0;
+    const uint32_t v0 = (uint32_t)(__shfl(pr1, q, 64) / K);
+    const uint32_t v1 = (uint32_t)(__shfl(pr1, 8 + q, 64) / K);
+    const size_t srow0 = (size_t)(st.pair / K) * SROW + 4 * SPW * wave;
+    const size_t srow1 = (size_t)(pr1 / K) * SROW + 4 * SPW * wave;
+    const uint32_t chunk = (uint32_t)((SPW * wave) * 128 + ((pos ^ q) << 4));
+    if (DUAL && act1 && st.un.w > 16) {  // (uniform)
+        if (dma) {
+#pragma unroll
+            for (int i = 0; i < SPW; ++i)
+                dma16(codes, cbytes, v0 * L + chunk + i * 128, (lds_ptr)(act1 + i * 2048));
+            if (st.un.w > 24) {  // (uniform)
+#pragma unroll
+                for (int i = 0; i < SPW; ++i)
+                    dma16(codes, cbytes, v1 * L + chunk + i * 128,
+                          (lds_ptr)(act1 + i * 2048 + 1024));
+            }
+        }
+        load_dwords<SPW>(scales + srow1, st.bs1);
+    }
     if (dma) {  // (uniform) else the area already holds this group
-        // lane r (< 16) holds the pair of the group's token r
-        const uint32_t t0 = (uint32_t)(__shfl(st.pair, q, 64) / K);
-        const uint32_t t1 = (uint32_t)(__shfl(st.pair, 8 + q, 64) / K);
-        const uint32_t chunk = (uint32_t)((SPW * wave) * 128 + ((pos ^ q) << 4));
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
             dma16(codes, cbytes, t0 * L + chunk + i * 128, (lds_ptr)(act + i * 2048));
@@ -251,15 +284,14 @@ __device__ __forceinline__ void up_issue_acts(UpStage<SPW>& st, int K, int n0,
                 dma16(codes, cbytes, t1 * L + chunk + i * 128, (lds_ptr)(act + i * 2048 + 1024));
         }
     }
-    const int t = st.pair / K;
-    load_dwords<SPW>(scales + (size_t)t * SROW + 4 * SPW * wave, st.bs);
+    load_dwords<SPW>(scales + srow0, st.bs);
 }
 
 // VMEM instructions of up_issue_weights (the pair id, SPW fragments and the scale dwords
 // of four tiles): a compute that follows the next item's weight issue waits with this
 // count for its own activations
-template <int SPW>
-constexpr int up_weight_loads() { return 1 + 4 * (SPW + SPW / 4 + (SPW % 4 ? 1 : 0)); }
+template <int SPW, bool DUAL>
+constexpr int up_weight_loads() { return (DUAL ? 2 : 1) + 4 * (SPW + SPW / 4 + (SPW % 4 ? 1 : 0)); }
 
 // Partial H tiles of the four wavefronts (each summed over its quarter of K), one buffer:
 // [wave][tile][token][row] FP32, tiles padded to 272 floats so that the gate and up reads
@@ -377,27 +409,40 @@ __device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, const uint8_t* act, 
 // caller stores it, before the next activation loads); later groups of a hot expert are
 // stored at once, and then the first group's too.
 // The first group's activations are followed by the next item's weight issue (and at
-// most the conditional ticket, which is older and completes with them).
-template <int SPW>
+// most the conditional ticket, which is older and completes with them).  The second
+// group's loads went out before the first group's (see up_issue_acts), so the second
+// group needs no wait; a third and later group (an expert of more than 32 tokens) loads
+// its activations into the second area and waits for every load in flight.
+template <int SPW, bool DUAL>
 __device__ __forceinline__ UpOut up_compute(UpStage<SPW>& st, int K, int I, bool store,
                                             const uint8_t* __restrict__ codes, int cbytes,
                                             const uint8_t* __restrict__ scales,
                                             const int32_t* __restrict__ pairs,
                                             uint8_t* __restrict__ hid,
                                             uint8_t* __restrict__ hid_scales, float* red,
-                                            int& rb, uint8_t* act, int* tick = nullptr,
-                                            int publish = 0) {
+                                            int& rb, uint8_t* act, uint8_t* act1,
+                                            int* tick = nullptr, int publish = 0) {
     const int r16 = threadIdx.x & 15;
-    UpOut first = up_group<SPW, up_weight_loads<SPW>()>(
+    UpOut first = up_group<SPW, up_weight_loads<SPW, DUAL>()>(
         st, act, 0, I, store, red + rb * RED_FLOATS, tick ? tick + rb : nullptr, publish);
     rb ^= 1;
     if (st.un.w <= 16) return first;
     up_store(first, hid, hid_scales);
     first.ok = false;
-    for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later token groups of a hot expert
+    int n0 = 16;
+    if (DUAL) {  // the second group is in act1 already
+        st.pair = st.pair1;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) st.bs[i] = st.bs1[i];
+        up_store(up_group<SPW, 63>(st, act1, 16, I, store, red + rb * RED_FLOATS), hid,
+                 hid_scales);
+        rb ^= 1;
+        n0 = 32;
+    }
+    for (; n0 < st.un.w; n0 += 16) {  // later token groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
-        up_issue_acts(st, K, n0, codes, cbytes, scales, act);
-        up_store(up_group<SPW, 0>(st, act, n0, I, store, red + rb * RED_FLOATS), hid,
+        up_issue_acts<SPW, DUAL>(st, K, n0, codes, cbytes, scales, act1);
+        up_store(up_group<SPW, 0>(st, act1, n0, I, store, red + rb * RED_FLOATS), hid,
                  hid_scales);
         rb ^= 1;
     }
@@ -432,7 +477,9 @@ __device__ __forceinline__ int take_ticket(unsigned* counters) {
 }
 __device__ __forceinline__ int ticket_item(int base, int t) { return base + 8 * t + (blockIdx.x & 7); }
 
-template <int SPW, bool PACKED>
+// DUAL: two activation areas a wavefront (the second token group's loads issued ahead);
+// else one (LDS then leaves room for a side-stream GEMM's workgroup on the same CU)
+template <int SPW, bool PACKED, bool DUAL>
 __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int K, int I, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const uint8_t* __restrict__ codes, int cbytes, const uint8_t* __restrict__ scales,
@@ -441,17 +488,25 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     uint8_t* __restrict__ hid_scales, unsigned* __restrict__ counter, int dyn) {
     __shared__ __attribute__((aligned(16))) float red[2 * RED_FLOATS];
     __shared__ int tick[2];
-    __shared__ int4 un_lds[1024];  // the first D units (one per touched expert), E <= 1024
-    // each wavefront's activation area (one token group; see up_issue_acts)
-    __shared__ __attribute__((aligned(1024))) uint8_t act_all[4][SPW * 2048];
-    uint8_t* act = act_all[threadIdx.x >> 6];
+    // the first D units (one per touched expert, E <= 1024) as (expert, begin, length)
+    __shared__ int un_lds[3 * 1024];
+    // each wavefront's activation areas (one token group each; see up_issue_acts); with
+    // one area, later groups reuse the first
+    __shared__ __attribute__((aligned(1024))) uint8_t act_all[DUAL ? 2 : 1][4][SPW * 2048];
+    uint8_t* act = act_all[0][threadIdx.x >> 6];
+    uint8_t* act1 = act_all[DUAL ? 1 : 0][threadIdx.x >> 6];
     const int nt = I / UP_COLS;
     const int D = num_units[2];
     const int items = D * nt;  // touched experts x column tiles
     const int G = gridDim.x;
     // the units in LDS: an item's unit is then an LDS read, not a global round trip
     // between learning the item and issuing its weight loads
-    for (int i = threadIdx.x; i < D; i += 256) un_lds[i] = units[i];
+    for (int i = threadIdx.x; i < D; i += 256) {
+        const int4 u = units[i];
+        un_lds[3 * i] = u.x;
+        un_lds[3 * i + 1] = u.y;
+        un_lds[3 * i + 2] = u.w;
+    }
     __syncthreads();
     int a = blockIdx.x;  // the item in stage A
     if (a >= items) return;
@@ -474,8 +529,10 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     int t_prev = 0;       // the ticket naming the next A (taken last pass, if dynamic)
     int rb = 0;
     UpStage<SPW> A, B;
-    up_issue_weights<SPW, PACKED>(A, item_of(a), nt, I, w13, s13, pairs, un_lds);
-    up_issue_acts(A, K, 0, codes, cbytes, scales, act);
+    // (B of A's expert: its groups are still in the areas up to this many tokens)
+    constexpr int REUSE = DUAL ? 32 : 16;
+    up_issue_weights<SPW, PACKED, DUAL>(A, item_of(a), nt, I, w13, s13, pairs, un_lds);
+    up_issue_acts<SPW, DUAL>(A, K, 0, codes, cbytes, scales, act, true, act1);
     // Items in pairs (stages A and B), pass k holding a_k and b_k.  Nothing between a
     // stage's loads and its compute is conditional: a conditional exit there would let the
     // compiler sink the loads below it, losing the prefetch.  Past the last item a stage
@@ -492,26 +549,27 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
         int* const tk = k + 1 < R ? nullptr : tick;
         // (the scheduling barriers keep each stage's loads ahead of the other stage's
         // compute; otherwise the scheduler interleaves them into it)
-        up_issue_weights<SPW, PACKED>(B, item_of(b_real ? b : a), nt, I, w13, s13, pairs,
-                                      un_lds);
+        up_issue_weights<SPW, PACKED, DUAL>(B, item_of(b_real ? b : a), nt, I, w13, s13, pairs,
+                                            un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        const UpOut oa = up_compute(A, K, I, true, codes, cbytes, scales, pairs, hid, hid_scales,
-                                    red, rb, act, tk, t_prev);
+        const UpOut oa = up_compute<SPW, DUAL>(A, K, I, true, codes, cbytes, scales, pairs, hid,
+                                               hid_scales, red, rb, act, act1, tk, t_prev);
         const int a_next = k + 1 < R ? a + 2 * G : ticket_item(base, oa.ticket);
         up_store(oa, hid, hid_scales);
         __builtin_amdgcn_sched_barrier(0);
-        // (B of A's expert, at most 16 tokens: its one group is still in the area)
-        up_issue_acts(B, K, 0, codes, cbytes, scales, act, !(B.un.x == A.un.x && A.un.w <= 16));
+        up_issue_acts<SPW, DUAL>(B, K, 0, codes, cbytes, scales, act,
+                                 !(B.un.x == A.un.x && A.un.w <= REUSE), act1);
         t_prev = k + 2 < R ? 0 : take_ticket(counter);  // names a_{k+2} if dynamic
         const int e_b = B.un.x;
-        up_issue_weights<SPW, PACKED>(A, item_of(a_next < items ? a_next : a), nt, I, w13, s13,
-                                      pairs, un_lds);
+        up_issue_weights<SPW, PACKED, DUAL>(A, item_of(a_next < items ? a_next : a), nt, I, w13,
+                                            s13, pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        const UpOut ob = up_compute(B, K, I, b_real, codes, cbytes, scales, pairs, hid,
-                                    hid_scales, red, rb, act, tk, t_b);
+        const UpOut ob = up_compute<SPW, DUAL>(B, K, I, b_real, codes, cbytes, scales, pairs,
+                                               hid, hid_scales, red, rb, act, act1, tk, t_b);
         up_store(ob, hid, hid_scales);
         __builtin_amdgcn_sched_barrier(0);
-        up_issue_acts(A, K, 0, codes, cbytes, scales, act, !(A.un.x == e_b && A.un.w <= 16));
+        up_issue_acts<SPW, DUAL>(A, K, 0, codes, cbytes, scales, act,
+                                 !(A.un.x == e_b && A.un.w <= REUSE), act1);
         __builtin_amdgcn_sched_barrier(0);
         if (a_next >= items) break;  // (every later item is larger)
         b = k + 1 < R ? b + 2 * G : ticket_item(base, ob.ticket);
@@ -579,8 +637,9 @@ struct DownStage {
     uint4 w[MT][IS];
     uint32_t sw[MT][IS];  // scale dwords of each row (byte g = K block 4s+g)
     uint32_t bs[IS];      // the hidden's scale dwords (the hidden itself goes through LDS)
+    uint32_t bs1[IS];     // those of the second token group (pairs 16..31 of the list)
     int4 un;
-    int j, pair;
+    int j, pair, pair1;   // pair ids of entries r and 16 + r of the expert's list
 };
 
 template <int IS, int MT, bool PACKED>
@@ -596,6 +655,7 @@ __device__ __forceinline__ void down_issue_weights(DownStage<IS, MT>& st, int it
     st.j = item - u * nt;
     st.un = units[u];
     st.pair = pairs[st.un.y + min(r16, st.un.w - 1)];
+    st.pair1 = pairs[st.un.y + min(16 + r16, st.un.w - 1)];
     const size_t R0 = (size_t)st.un.x * L + st.j * (64 * MT) + wave * (16 * MT) + r16;
     // packed layout: this wavefront's fragments are MT*IS consecutive 1 KiB blocks in
     // lane order (the scale rows keep their order)
@@ -618,32 +678,47 @@ __device__ __forceinline__ void down_issue_weights(DownStage<IS, MT>& st, int it
 // chunk c at position c ^ (r & 7), as in the up projection), eight whole 128-byte rows
 // per direct load, the second eight skipped for groups of at most eight tokens.  Rows past
 // the group's last token hold its last token.  The scale dwords are register loads.
+// hb1 (the first group's call only): an expert of more than 16 pairs also gets its second
+// group's hidden, into the stage's second buffer hb1, and its scale dwords (bs1) -- issued
+// BEFORE the first group's loads, so that the first group's exact wait (and barrier)
+// covers them and the second group is computed without draining the next item's weights.
+// Every address is computed before any branch (one wait for the pair ids on every path).
 template <int IS, int MT>
 __device__ __forceinline__ void down_issue_acts(DownStage<IS, MT>& st, int n0,
                                                 const uint8_t* __restrict__ hid, int hbytes,
                                                 const uint8_t* __restrict__ hid_scales,
-                                                uint8_t* hb) {
+                                                uint8_t* hb, uint8_t* hb1 = nullptr) {
     constexpr int I = IS * 128, SROW = I / 32;
     const int lane = threadIdx.x & 63;
     // the wavefront index as a scalar: the branch and the LDS base are then uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 3, pos = lane & 7;
-    if (wave < IS) {
-        const uint32_t chunk = (uint32_t)(wave * 128 + ((pos ^ q) << 4));
-        const uint32_t p0 = (uint32_t)__shfl(st.pair, q, 64);
-        dma16(hid, hbytes, p0 * I + chunk, (lds_ptr)(hb + wave * 2048));
-        if (st.un.w - n0 > 8) {  // (uniform)
-            const uint32_t p1 = (uint32_t)__shfl(st.pair, 8 + q, 64);
-            dma16(hid, hbytes, p1 * I + chunk, (lds_ptr)(hb + wave * 2048 + 1024));
+    const uint32_t chunk = (uint32_t)(wave * 128 + ((pos ^ q) << 4));
+    const uint32_t p0 = (uint32_t)__shfl(st.pair, q, 64);
+    const uint32_t p1 = (uint32_t)__shfl(st.pair, 8 + q, 64);
+    const uint32_t r0 = (uint32_t)__shfl(st.pair1, q, 64);
+    const uint32_t r1 = (uint32_t)__shfl(st.pair1, 8 + q, 64);
+    const size_t srow0 = (size_t)st.pair * SROW, srow1 = (size_t)st.pair1 * SROW;
+    if (hb1 && st.un.w > 16) {  // (uniform)
+        if (wave < IS) {
+            dma16(hid, hbytes, r0 * I + chunk, (lds_ptr)(hb1 + wave * 2048));
+            if (st.un.w > 24)  // (uniform)
+                dma16(hid, hbytes, r1 * I + chunk, (lds_ptr)(hb1 + wave * 2048 + 1024));
         }
+        load_dwords<IS>(hid_scales + srow1, st.bs1);
     }
-    load_dwords<IS>(hid_scales + (size_t)st.pair * SROW, st.bs);
+    if (wave < IS) {
+        dma16(hid, hbytes, p0 * I + chunk, (lds_ptr)(hb + wave * 2048));
+        if (st.un.w - n0 > 8)  // (uniform)
+            dma16(hid, hbytes, p1 * I + chunk, (lds_ptr)(hb + wave * 2048 + 1024));
+    }
+    load_dwords<IS>(hid_scales + srow0, st.bs);
 }
 
 // VMEM instructions of down_issue_weights (the pair id, MT*IS fragments and MT rows of
 // scale dwords): a compute that follows the next item's weight issue waits with this count
 template <int IS, int MT>
-constexpr int down_weight_loads() { return 1 + MT * IS + MT * (IS / 4 + (IS % 4 ? 1 : 0)); }
+constexpr int down_weight_loads() { return 2 + MT * IS + MT * (IS / 4 + (IS % 4 ? 1 : 0)); }
 
 // The wavefront's output block is 16 tokens x 16*MT columns of BF16.  It is staged in
 // the wavefront's own LDS area ([token][column], rows padded by 16 bytes) and written
@@ -717,24 +792,30 @@ __device__ __forceinline__ void down_store(const DownStage<IS, MT>& st, int n0, 
 // The item's first token group is computed and left staged (the caller stores it, before
 // the next activation loads); later groups of a hot expert are stored at once.
 // The first group's hidden is followed by the next item's weight issue (and at most the
-// conditional ticket, older).  A later group reuses the buffer once every wavefront is
-// done reading the one before (a barrier ahead of its loads).
+// conditional ticket, older).  The second group's hidden is already in hb1 (see
+// down_issue_acts); a third and later group reuses hb1 once every wavefront is done
+// reading it (a barrier ahead of its loads) and waits for every load in flight.
 template <int IS, int MT>
 __device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L, bool store,
                                              const uint8_t* __restrict__ hid, int hbytes,
                                              const uint8_t* __restrict__ hid_scales,
                                              const int32_t* __restrict__ pairs,
                                              uint16_t* __restrict__ rows, uint8_t* hb,
-                                             uint8_t* stage) {
+                                             uint8_t* hb1, uint8_t* stage) {
     const int r16 = threadIdx.x & 15;
     down_mfma_stage<IS, MT, down_weight_loads<IS, MT>()>(st, hb, min(st.un.w, 16), stage);
     if (st.un.w <= 16) return;
     down_store(st, 0, L, store, rows, stage);
-    for (int n0 = 16; n0 < st.un.w; n0 += 16) {  // later pair groups of a hot expert
+    st.pair = st.pair1;
+#pragma unroll
+    for (int i = 0; i < IS; ++i) st.bs[i] = st.bs1[i];
+    down_mfma_stage<IS, MT, 63>(st, hb1, min(st.un.w - 16, 16), stage);
+    down_store(st, 16, L, store, rows, stage);
+    for (int n0 = 32; n0 < st.un.w; n0 += 16) {  // later pair groups of a hot expert
         st.pair = pairs[st.un.y + min(n0 + r16, st.un.w - 1)];
         lds_sync();
-        down_issue_acts(st, n0, hid, hbytes, hid_scales, hb);
-        down_mfma_stage<IS, MT, 0>(st, hb, min(st.un.w - n0, 16), stage);
+        down_issue_acts(st, n0, hid, hbytes, hid_scales, hb1);
+        down_mfma_stage<IS, MT, 0>(st, hb1, min(st.un.w - n0, 16), stage);
         down_store(st, n0, L, store, rows, stage);
     }
 }
@@ -747,8 +828,10 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     const int32_t* __restrict__ num_units, uint16_t* __restrict__ rows,
     unsigned* __restrict__ counter, int dyn, int hbytes) {
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][16 * (32 * MT + 16)];
-    // the hidden of stage A's and stage B's current token group (see down_issue_acts)
+    // the hidden of stage A's and stage B's first and second token groups (see
+    // down_issue_acts)
     __shared__ __attribute__((aligned(1024))) uint8_t hbuf[2][IS * 2048];
+    __shared__ __attribute__((aligned(1024))) uint8_t hbuf1[2][IS * 2048];
     __shared__ int tick[2];
     __shared__ int4 un_lds[1024];  // the first D units, as in the up projection
     uint8_t* stage = stage_all[threadIdx.x >> 6];
@@ -766,7 +849,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     int t_prev = 0;
     DownStage<IS, MT> A, B;
     down_issue_weights<IS, MT, PACKED>(A, a, nt, L, w2, s2, pairs, un_lds);
-    down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0]);
+    down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0], hbuf1[0]);
     // items in pairs, nothing conditional between a stage's loads and its compute, each
     // stage's stores right after its compute (see the up projection); the dynamic tail's
     // tickets as there, published through one barrier a stage
@@ -775,7 +858,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         const int t_b = k + 1 < R ? 0 : take_ticket(counter);
         down_issue_weights<IS, MT, PACKED>(B, b_real ? b : a, nt, L, w2, s2, pairs, un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        down_compute(A, L, true, hid, hbytes, hid_scales, pairs, rows, hbuf[0], stage);
+        down_compute(A, L, true, hid, hbytes, hid_scales, pairs, rows, hbuf[0], hbuf1[0], stage);
         int a_next = a + 2 * G;
         if (k + 1 >= R) {  // uniform
             if (threadIdx.x == 0) tick[0] = t_prev;
@@ -784,12 +867,13 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         }
         if (A.un.w <= 16) down_store(A, 0, L, true, rows, stage);
         __builtin_amdgcn_sched_barrier(0);
-        down_issue_acts(B, 0, hid, hbytes, hid_scales, hbuf[1]);
+        down_issue_acts(B, 0, hid, hbytes, hid_scales, hbuf[1], hbuf1[1]);
         t_prev = k + 2 < R ? 0 : take_ticket(counter);
         down_issue_weights<IS, MT, PACKED>(A, a_next < items ? a_next : a, nt, L, w2, s2, pairs,
                                            un_lds);
         __builtin_amdgcn_sched_barrier(0);
-        down_compute(B, L, b_real, hid, hbytes, hid_scales, pairs, rows, hbuf[1], stage);
+        down_compute(B, L, b_real, hid, hbytes, hid_scales, pairs, rows, hbuf[1], hbuf1[1],
+                     stage);
         int b_next = b + 2 * G;
         if (k + 1 >= R) {
             if (threadIdx.x == 0) tick[1] = t_b;
@@ -798,7 +882,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         }
         if (B.un.w <= 16) down_store(B, 0, L, b_real, rows, stage);
         __builtin_amdgcn_sched_barrier(0);
-        down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0]);
+        down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0], hbuf1[0]);
         __builtin_amdgcn_sched_barrier(0);
         if (a_next >= items) break;
         a = a_next;
@@ -887,6 +971,7 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          bool counters_zeroed, hipStream_t s) {
     (void)unit;
     const int dyn = T <= kDynTailTokens ? 1 : 0;
+    const bool dual = T >= kUpTwoAreaTokens;
     if (dyn && !counters_zeroed)
         hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, counters, 16);
     const int4* un = (const int4*)units;
@@ -899,18 +984,25 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
     // packed weights exist only for L % 512 == 0 and I / 128 in {1, 2, 4} (checked by the
     // callers), which the fast kernels cover
     switch ((stages & 1) ? (L % 512 == 0 ? L / 512 : 0) : -1) {
+#define MOE_UP_L(SPW, DUAL)                                                                  \
+    if (packed)                                                                              \
+        hipLaunchKernelGGL((k_ffn_up_fast<SPW, true, DUAL>), ugrid, blk, 0, s, K, I, w13,    \
+                           s13, codes, cbytes, scales, pairs, un, num_units, hid, hsc,       \
+                           counters, dyn);                                                   \
+    else                                                                                     \
+        hipLaunchKernelGGL((k_ffn_up_fast<SPW, false, DUAL>), ugrid, blk, 0, s, K, I, w13,   \
+                           s13, codes, cbytes, scales, pairs, un, num_units, hid, hsc,       \
+                           counters, dyn);
 #define MOE_UP(SPW)                                                                          \
     case SPW:                                                                                \
-        if (packed)                                                                          \
-            hipLaunchKernelGGL((k_ffn_up_fast<SPW, true>), ugrid, blk, 0, s, K, I, w13, s13, \
-                               codes, cbytes, scales, pairs, un, num_units, hid, hsc,        \
-                               counters, dyn);                                               \
-        else                                                                                 \
-            hipLaunchKernelGGL((k_ffn_up_fast<SPW, false>), ugrid, blk, 0, s, K, I, w13, s13,\
-                               codes, cbytes, scales, pairs, un, num_units, hid, hsc,        \
-                               counters, dyn);                                               \
+        if (dual) {                                                                          \
+            MOE_UP_L(SPW, true)                                                              \
+        } else {                                                                             \
+            MOE_UP_L(SPW, false)                                                             \
+        }                                                                                    \
         break;
         MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7)
+#undef MOE_UP_L
 #undef MOE_UP
         case -1:
             break;

@@ -26,11 +26,12 @@ __device__ __forceinline__ void load_slots(int t, int K, const float* __restrict
             const int4 d = ids ? ((const int4*)(ids + (size_t)t * 16))[i] : make_int4(0, 0, 0, 0);
             id[4 * i] = d.x, id[4 * i + 1] = d.y, id[4 * i + 2] = d.z, id[4 * i + 3] = d.w;
         }
-    } else {
+    } else {  // unconditional loads of a clamped slot, batched; slots past K dropped below
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            wk[k] = k < K ? w[(size_t)t * K + k] : 0.0f;
-            id[k] = (k < K && ids) ? ids[(size_t)t * K + k] : 0;
+            const size_t i = (size_t)t * K + (k < K ? k : K - 1);
+            wk[k] = w[i];
+            id[k] = ids ? ids[i] : 0;
         }
     }
 #pragma unroll
@@ -45,11 +46,25 @@ __global__ __launch_bounds__(1024) void k_finalize(int K, int cols8, const uint4
     float wk[16];
     bool ok[16];
     load_slots(t, K, w, ids, wk, ok);
+    // An invalid slot loads the first valid slot's row instead (and drops it), so every
+    // row load is unconditional and the K of them go out as one batch, while the row of
+    // an invalid slot is still never read.  A token with no valid slot reads no row.
+    int first = -1;
+#pragma unroll
+    for (int k = 15; k >= 0; --k) first = ok[k] ? k : first;
+    if (first < 0) {
+        for (int c = threadIdx.x; c < cols8; c += blockDim.x)
+            out[(size_t)t * cols8 + c] = make_uint4(0, 0, 0, 0);
+        return;
+    }
+    int src[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) src[k] = ok[k] ? k : first;
     for (int c = threadIdx.x; c < cols8; c += blockDim.x) {
         uint4 v[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-            v[k] = ok[k] ? rows[((size_t)t * K + k) * cols8 + c] : make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < 16; ++k) v[k] = rows[((size_t)t * K + src[k]) * cols8 + c];
+        __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first multiply-add
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;

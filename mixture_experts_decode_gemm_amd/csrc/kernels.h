@@ -53,6 +53,10 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
 // with a small kernel).  In moe_grouped_ffn's workspace they sit at ffn_counter_offset.
 size_t ffn_counter_offset(int P, int I);
 constexpr int kDynTailTokens = 256;
+// From kUpTwoAreaTokens tokens the gate/up pass keeps two activation areas a wavefront
+// (an expert's second token group loaded ahead with its first); below, one (less LDS, so
+// that its workgroups share CUs with the side stream's GEMMs)
+constexpr int kUpTwoAreaTokens = 128;
 // the packed expert layout (see ffn.hip); L % 512 == 0, I / 128 in {1, 2, 4}
 hipError_t launch_pack_experts(int E, int L, int I, const uint8_t* w13, const uint8_t* s13,
                                const uint8_t* w2, const uint8_t* s2, uint8_t* pw13, uint8_t* ps13,

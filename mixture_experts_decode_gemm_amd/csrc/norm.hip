@@ -62,24 +62,36 @@ __global__ __launch_bounds__(1024) void k_finalize_rmsnorm(int K, int cols8,
     __shared__ float part[16];
     const int t = blockIdx.x, c = threadIdx.x;
     const bool live = c < cols8;
+    // Every load is unconditional, from a clamped slot and column, so the K row fragments
+    // and the norm weights go out as one batch with no branch between them (a load behind
+    // a branch can get a wait of its own: one more round trip).  Slots past K and lanes
+    // past the row end load a valid address and their values are dropped below.
+    const int cc = live ? c : cols8 - 1;
+    const uint4 gw = g[cc];
     uint4 v[16];
     float wk[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        wk[k] = k < K ? w[t * K + k] : 0.0f;
-        v[k] = (k < K && live) ? rows[(size_t)(t * K + k) * cols8 + c] : make_uint4(0, 0, 0, 0);
+        const int kk = k < K ? k : K - 1;
+        wk[k] = w[t * K + kk];
+        v[k] = rows[(size_t)(t * K + kk) * cols8 + cc];
     }
+    __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first multiply-add
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    // slots past K keep the sum as it was (a select, not a branch: behind a branch the
+    // compiler sinks each weight's scalar load there and waits for it one slot at a time)
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        if (k >= K) continue;
+        const bool use = k < K;
         const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = __builtin_fmaf(wk[k], bf16_lo(q[i]), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(wk[k], bf16_hi(q[i]), acc[2 * i + 1]);
+            const float a = __builtin_fmaf(wk[k], bf16_lo(q[i]), acc[2 * i]);
+            const float b = __builtin_fmaf(wk[k], bf16_hi(q[i]), acc[2 * i + 1]);
+            acc[2 * i] = use ? a : acc[2 * i];
+            acc[2 * i + 1] = use ? b : acc[2 * i + 1];
         }
     }
     uint32_t o[4];
@@ -92,6 +104,7 @@ __global__ __launch_bounds__(1024) void k_finalize_rmsnorm(int K, int cols8,
         ss = __builtin_fmaf(a, a, ss);
         ss = __builtin_fmaf(b, b, ss);
     }
+    ss = live ? ss : 0.f;
     if (live) routed[(size_t)t * cols8 + c] = make_uint4(o[0], o[1], o[2], o[3]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
@@ -101,7 +114,6 @@ __global__ __launch_bounds__(1024) void k_finalize_rmsnorm(int K, int cols8,
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
     const float inv = 1.0f / sqrtf(tot / (float)(cols8 * 8) + eps);
     if (!live) return;
-    const uint4 gw = g[c];
     const uint32_t h[4] = {gw.x, gw.y, gw.z, gw.w};
     uint32_t n[4];
 #pragma unroll

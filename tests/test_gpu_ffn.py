@@ -99,6 +99,47 @@ def test_ffn_mx_full_size_multi_unit(orc):
     check_mx(orc, d, w, codes, scales, ids, sample)
 
 
+def grouped_ids(counts, K):
+    """ids [T, K] in which expert e is chosen by exactly counts[e] tokens (T = sum / K):
+    the sorted expert labels dealt round-robin, so that a token's K slots lie T apart in
+    the sorted order and name K distinct experts (every count is below T)."""
+    labels = np.repeat(np.arange(len(counts)), counts)
+    T = len(labels) // K
+    assert T * K == len(labels) and max(counts) < T
+    return np.stack([labels[T * k:T * (k + 1)] for k in range(K)], axis=1).astype(np.int32)
+
+
+def test_ffn_mx_token_groups_every_pair(orc):
+    """Experts whose lists end on each side of the token-group boundaries of the expert
+    passes (16 tokens per MFMA column tile, the second group's loads issued ahead with the
+    first's, a third and later group loaded on their own; 8 of a group's tokens per direct
+    load): every pair's hidden and rows against the oracle, at 512 gate/up items (two full
+    passes of 256 workgroups, whose two stages take neighbouring column tiles of one
+    expert, the second reusing the first's activations); and the packed weights' run bit
+    for bit equal to the row-major one."""
+    counts = [1, 7, 8, 9, 15, 16, 17, 20, 24, 25, 28, 32, 33, 40, 48, 49] * 2
+    K, L, I = 4, 512, 512
+    ids = grouped_ids(counts, K)
+    T, E = ids.shape[0], len(counts)
+    say(f"ffn mx token groups T={T} K={K} E={E} L={L} I={I}")
+    assert (np.bincount(ids.ravel(), minlength=E) == counts).all()
+    w = syn.expert_weights(dict(L=L, I=I, E=E, expert_format=0), seed=8)
+    codes, scales = mx_latent(orc, syn.rng(8, 704), T, L)
+    d = moe.dims(T, T, hidden=256, latent=L, experts=E, top_k=K, expert_inter=I)
+    check_mx(orc, d, w, codes, scales, ids, np.arange(T * K, dtype=np.int32))
+    ref_rows, ref_hid, _ = run_ffn_mx(d, w, codes, scales, ids)
+    pk = moe.moe_pack_expert_weights(d, dev(w["w13"]), dev(w["s13"]), dev(w["w2"]), dev(w["s2"]))
+    dp = moe.dims(T, T, hidden=256, latent=L, experts=E, top_k=K, expert_inter=I,
+                  expert_format=moe.MOE_FMT_MXFP4_MXFP8_PACKED)
+    pairs, units, nu = build_lists(dp, dev(ids))
+    rows = torch.zeros(T * K, L, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(moe.moe_ffn_workspace_size(dp), dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_ffn(dp, *pk, dev(codes), dev(scales), pairs, units, nu, rows, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ws[:T * K * I]).reshape(T * K, I), ref_hid)
+    assert np.array_equal(host(rows), ref_rows)
+
+
 def test_ffn_stages_match_grouped():
     """The up pass then the down pass, as two calls, give the one-call result bit for bit."""
     T, K, E, L, I = 40, 4, 12, 512, 256

@@ -487,13 +487,16 @@ def bench_finalize(torch, moe, stream, time_calls, steps):
 def bench_router_front(torch, moe, syn, stream, time_calls, steps, dev):
     """The routing front at 1020 tokens: router GEMM (x [1020, 7168] x W_gate [896, 7168],
     FP32 logits), sigmoid top-16 with the correction bias, lists and unit windows;
-    uniform and Zipf routing bias; ROTATE_SETS sets of x and W_gate (275 MB)."""
+    uniform and Zipf routing bias; ROTATE_SETS sets of x and W_gate (275 MB).  W_gate is in
+    the packed layout, as the layer's dense weights are (prepared once, ahead of the
+    steps); the row-major W_gate's router time is reported beside it."""
     T, H, E = 1020, 7168, 896
     g = torch.Generator(device="cuda").manual_seed(3)
     xs = [torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
           for _ in range(ROTATE_SETS)]
-    wgs = [(torch.randn(E, H, generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
+    wrm = [(torch.randn(E, H, generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
            for _ in range(ROTATE_SETS)]
+    wgs = [moe.moe_pack_dense_weight(w) for w in wrm]
     d = moe.dims(T, T)
     logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
     ids = torch.empty(T, 16, dtype=torch.int32, device="cuda")
@@ -515,7 +518,13 @@ def bench_router_front(torch, moe, syn, stream, time_calls, steps, dev):
 
         def topk(i=0, b=b):
             j = i % ROTATE_SETS
-            moe.moe_router_topk(d, xs[j], wgs[j], b, logits, ids, wts, workspace=rws, stream=stream)
+            moe.moe_router_topk(d, xs[j], wgs[j], b, logits, ids, wts,
+                                flags=moe.MOE_GATE_PACKED, workspace=rws, stream=stream)
+
+        def topk_rm(i=0, b=b):
+            j = i % ROTATE_SETS
+            moe.moe_router_topk(d, xs[j], wrm[j], b, logits, ids, wts, workspace=rws,
+                                stream=stream)
 
         def lists(i=0):
             moe.moe_build_lists(d, ids, counts, offsets, pairs, units, nu, lws, stream=stream)
@@ -523,11 +532,13 @@ def bench_router_front(torch, moe, syn, stream, time_calls, steps, dev):
         def both(i=0, b=b):
             topk(i, b)
             lists(i)
+        t_topk_rm = time_calls(topk_rm, max(steps, 20) * ROTATE_SETS)
         t_topk = time_calls(topk, max(steps, 20) * ROTATE_SETS)
         t_lists = time_calls(lists, max(steps, 20) * ROTATE_SETS)
         t_both = time_calls(both, max(steps, 20) * ROTATE_SETS)
         torch.cuda.synchronize()
-        res[name] = {"router_gemm_topk_us": t_topk, "lists_us": t_lists, "front_us": t_both,
+        res[name] = {"router_gemm_topk_us": t_topk, "router_gemm_topk_row_major_us": t_topk_rm,
+                     "lists_us": t_lists, "front_us": t_both,
                      "touched_experts": int(torch.count_nonzero(counts).item()),
                      "units": int(nu[0].item())}
     return res

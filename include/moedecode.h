@@ -61,7 +61,10 @@ enum { MOE_FMT_MXFP4_MXFP8 = 0, /* MXFP4 (E2M1 + E8M0 per 32) weights x MXFP8 (E
                                    the packed layout of moe_pack_expert_weights */
 
 /* moe_router_topk flags */
-enum { MOE_LOGITS_GIVEN = 1 }; /* skip the router GEMM and read `logits` as input */
+enum {
+    MOE_LOGITS_GIVEN = 1, /* skip the router GEMM and read `logits` as input */
+    MOE_GATE_PACKED = 2   /* w_gate in the packed layout of moe_pack_dense_weight */
+};
 
 /* Host struct describing the layer.  tokens = T of this call; max_tokens sizes the
    workspace (the widest batch, as [wide] WideScratch sizes its buffers).
@@ -118,7 +121,10 @@ typedef struct {
    in descending order, ties to the lower expert id -> ids [T,K] int32; weights [T,K] FP32
    = the chosen unbiased scores, divided by their slot-order FP32 sum when renormalize,
    times routed_scale.  workspace: >= moe_router_workspace_size(d) bytes (split-K
-   partials of the GEMM; may be NULL when MOE_LOGITS_GIVEN). */
+   partials of the GEMM; may be NULL when MOE_LOGITS_GIVEN).  MOE_GATE_PACKED: w_gate
+   holds the packed layout of moe_pack_dense_weight (as the layer's dense weights may;
+   needs experts % 64 == 0 and hidden % 128 == 0, else MOE_ERR_FORMAT); the logits are
+   the same bits as from the row-major W_gate. */
 moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
                            const float* bias, float* logits, int32_t* ids, float* weights,
                            int32_t flags, void* workspace, size_t ws_bytes, void* stream);

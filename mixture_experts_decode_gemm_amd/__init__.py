@@ -20,6 +20,7 @@ STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_ALIGN", "MOE
                 "MOE_ERR_FORMAT", "MOE_ERR_LAUNCH"]
 MOE_FMT_MXFP4_MXFP8, MOE_FMT_BF16, MOE_FMT_MXFP4_MXFP8_PACKED = 0, 1, 2
 MOE_LOGITS_GIVEN = 1
+MOE_GATE_PACKED = 2
 MOE_LINEAR_F32, MOE_LINEAR_BF16, MOE_LINEAR_ADD_BF16 = 0, 1, 2
 MOE_DENSE_ROWMAJOR, MOE_DENSE_PACKED = 0, 1
 WORKSPACE_FIELDS = ["logits", "ids", "weights", "counts", "offsets", "pairs", "units", "num_units",

@@ -206,8 +206,11 @@ moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
                            int32_t flags, void* workspace, size_t ws_bytes, void* stream) {
     moe_status st = check_dims(d);
     if (st != MOE_OK) return st;
-    if (flags & ~MOE_LOGITS_GIVEN) return MOE_ERR_FORMAT;
+    if (flags & ~(MOE_LOGITS_GIVEN | MOE_GATE_PACKED)) return MOE_ERR_FORMAT;
     const bool given = flags & MOE_LOGITS_GIVEN;
+    const bool packed = !given && (flags & MOE_GATE_PACKED);
+    if (packed && !wgemm_fits(d->max_tokens, d->experts, d->experts, d->experts, d->hidden, true))
+        return MOE_ERR_FORMAT;
     if (!bias || !logits || !ids || !weights) return MOE_ERR_NULL;
     if (!given && (!x || !w_gate)) return MOE_ERR_NULL;
     if (!al16(bias) || !al16(logits) || !al16(ids) || !al16(weights)) return MOE_ERR_ALIGN;
@@ -216,14 +219,17 @@ moe_status moe_router_topk(const moe_dims* d, const void* x, const void* w_gate,
     if (need && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
     if (workspace && !al16(workspace)) return MOE_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (!given && router_fast(d)) {
+    if (!given && (packed || router_fast(d))) {
+        // the split partials are added (in split order) into each token's logits inside the
+        // top-K launch, as in the layer's front: no separate reduce, no logits round trip
         int S = 1;
         if (launch_wgemm(d->tokens, d->experts, d->experts, d->experts, d->hidden, x, w_gate,
-                         nullptr, nullptr, false, (float*)workspace, s, false, &S) != hipSuccess ||
-            launch_wg_reduce(d->tokens, d->experts, d->experts, d->experts, S,
-                             (const float*)workspace, logits, 0, nullptr, nullptr, s,
-                             false) != hipSuccess)
+                         nullptr, nullptr, packed, (float*)workspace, s, false, &S) != hipSuccess)
             return MOE_ERR_LAUNCH;
+        return launch_status(launch_front_topk(d->tokens, d->experts, d->experts, 0, S,
+                                               (const float*)workspace, logits, bias, d->top_k,
+                                               d->renormalize, d->routed_scale, ids, weights,
+                                               nullptr, nullptr, nullptr, nullptr, s));
     } else if (!given) {
         hipError_t e = launch_gemm(d->tokens, d->experts, d->hidden, x, w_gate, logits, nullptr, 0,
                                    workspace, s);

@@ -127,7 +127,12 @@ def test_quant_rejects(L):
 def test_router_rejects(L):
     d = good_dims()
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
-    assert L.moe_router_topk(C.byref(d), *args, 2, FAKE, 1 << 40, None) == moe.MOE_ERR_FORMAT
+    assert L.moe_router_topk(C.byref(d), *args, 4, FAKE, 1 << 40, None) == moe.MOE_ERR_FORMAT
+    # a packed W_gate needs experts % 64 == 0
+    d32 = good_dims()
+    d32.experts, d32.top_k = 32, 4
+    assert L.moe_router_topk(C.byref(d32), *args, moe.MOE_GATE_PACKED, FAKE, 1 << 40,
+                             None) == moe.MOE_ERR_FORMAT
     need = moe.moe_router_workspace_size(d)
     assert need > 0
     assert L.moe_router_topk(C.byref(d), *args, 0, FAKE, 16, None) == moe.MOE_ERR_WORKSPACE

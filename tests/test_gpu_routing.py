@@ -48,10 +48,10 @@ def check_lists(orc, d, ids):
     return got
 
 
-@pytest.mark.parametrize("zipf", [False, True])
-def test_router_front_1020(orc, zipf):
+@pytest.mark.parametrize("zipf,packed", [(False, False), (True, False), (False, True)])
+def test_router_front_1020(orc, zipf, packed):
     T, E, H, K = 1020, 896, 7168, 16
-    say(f"router front T={T} zipf={zipf}")
+    say(f"router front T={T} zipf={zipf} packed={packed}")
     x = syn.router_input(T, H, seed=0)
     wg = syn.bf16_normal(syn.rng(0, 1), (E, H), 1 / np.sqrt(H))
     bias = syn.routing_bias(E, 1 if zipf else 0, zipf)
@@ -60,7 +60,17 @@ def test_router_front_1020(orc, zipf):
     ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
     w = torch.empty(T, K, dtype=torch.float32, device="cuda")
     ws = torch.empty(moe.moe_router_workspace_size(d), dtype=torch.uint8, device="cuda")
-    moe.moe_router_topk(d, dev(x), dev(wg), dev(bias), logits, ids, w, workspace=ws)
+    if packed:  # the packed W_gate gives the row-major run's logits bit for bit
+        moe.moe_router_topk(d, dev(x), dev(wg), dev(bias), logits, ids, w, workspace=ws)
+        torch.cuda.synchronize()
+        lg_rm = host(logits).copy()
+        logits.fill_(0)
+        moe.moe_router_topk(d, dev(x), moe.moe_pack_dense_weight(dev(wg)), dev(bias), logits,
+                            ids, w, flags=moe.MOE_GATE_PACKED, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(logits).view(np.uint32), lg_rm.view(np.uint32))
+    else:
+        moe.moe_router_topk(d, dev(x), dev(wg), dev(bias), logits, ids, w, workspace=ws)
     torch.cuda.synchronize()
     lg = host(logits)
     sample = np.r_[0:4, 500:504, T - 4:T]

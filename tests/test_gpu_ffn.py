@@ -109,15 +109,18 @@ def grouped_ids(counts, K):
     return np.stack([labels[T * k:T * (k + 1)] for k in range(K)], axis=1).astype(np.int32)
 
 
-def test_ffn_mx_token_groups_every_pair(orc):
+# 32 experts, 186 tokens: the two-area gate/up build (from 128 tokens) at 512 items; 16
+# experts, 93 tokens: the one-area build, whose later groups reload the one area
+@pytest.mark.parametrize("copies", [2, 1])
+def test_ffn_mx_token_groups_every_pair(orc, copies):
     """Experts whose lists end on each side of the token-group boundaries of the expert
     passes (16 tokens per MFMA column tile, the second group's loads issued ahead with the
     first's, a third and later group loaded on their own; 8 of a group's tokens per direct
     load): every pair's hidden and rows against the oracle, at 512 gate/up items (two full
     passes of 256 workgroups, whose two stages take neighbouring column tiles of one
-    expert, the second reusing the first's activations); and the packed weights' run bit
-    for bit equal to the row-major one."""
-    counts = [1, 7, 8, 9, 15, 16, 17, 20, 24, 25, 28, 32, 33, 40, 48, 49] * 2
+    expert, the second reusing the first's activations) or 256; and the packed weights'
+    run bit for bit equal to the row-major one."""
+    counts = [1, 7, 8, 9, 15, 16, 17, 20, 24, 25, 28, 32, 33, 40, 48, 49] * copies
     K, L, I = 4, 512, 512
     ids = grouped_ids(counts, K)
     T, E = ids.shape[0], len(counts)

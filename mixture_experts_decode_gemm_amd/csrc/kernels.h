@@ -27,7 +27,7 @@ hipError_t launch_front_topk(int T, int N, int E, int L, int S, const float* par
                              uint8_t* scales, hipStream_t s);
 
 // routing lists: scratch of lists_scratch_bytes(T, E) bytes, which ends with the slot map
-// (lists_slot_map) that launch_topk fills; slot_of null: the fill finds the slots in ids
+// (lists_slot_map) that launch_topk fills; slot_of null: the mark launch fills it
 size_t lists_scratch_bytes(int T, int E);
 uint8_t* lists_slot_map(void* scratch, int T, int E);
 // whether launch_lists builds the lists in one workgroup (no slot map needed then)

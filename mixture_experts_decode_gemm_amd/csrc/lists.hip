@@ -11,8 +11,9 @@
 //            exclusive prefix sums over experts (offsets, window indices), the units
 //            (the first window of every touched expert first, then the later windows);
 //   fill  -- one thread per (word, expert): the set bits in ascending token order give
-//            the list entries; the slot k is the one the top-K recorded in the slot map
-//            (the layer's path), else the first slot of that token holding e.
+//            the list entries; the slot k comes from the slot map, recorded by the top-K
+//            (the layer's path) or by the mark launch (the first slot of the token
+//            holding e).
 // Lists therefore hold ascending pair ids.  Batches whose bitmaps fit in LDS take one
 // launch instead (k_lists_fused).
 #include "device.h"
@@ -31,9 +32,13 @@ uint8_t* lists_slot_map(void* scratch, int T, int E) {
     return (uint8_t*)scratch + 2 * W * (size_t)E * sizeof(uint32_t);
 }
 
+// slot_map (optional): also records the slot map the fill reads -- one thread per token,
+// slots written last to first, so that an expert a token names twice keeps its first slot
+// (the list holds one pair per token and expert)
 __global__ __launch_bounds__(256) void k_lists_mark(int T, int K, int E,
                                                     const int32_t* __restrict__ ids,
-                                                    uint32_t* __restrict__ bm) {
+                                                    uint32_t* __restrict__ bm,
+                                                    uint8_t* __restrict__ slot_map) {
     wave_priority_high();
     __shared__ uint32_t words[1024];
     const int w = blockIdx.x;
@@ -44,6 +49,15 @@ __global__ __launch_bounds__(256) void k_lists_mark(int T, int K, int E,
     for (int q = threadIdx.x; q < n; q += 256) {
         const int e = ids[(size_t)t0 * K + q];
         if (e >= 0 && e < E) atomicOr(&words[e], 1u << (q / K));
+    }
+    if (slot_map && (int)threadIdx.x < min(32, T - t0)) {
+        const int t = t0 + threadIdx.x;
+        int32_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = ids[(size_t)t * K + min(k, K - 1)];  // (together)
+#pragma unroll
+        for (int k = 15; k >= 0; --k)
+            if (k < K && v[k] >= 0 && v[k] < E) slot_map[(size_t)t * E + v[k]] = (uint8_t)k;
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) bm[(size_t)w * E + e] = words[e];
@@ -133,7 +147,6 @@ __global__ __launch_bounds__(1024) void k_lists_scan(int T, int K, int E, int un
 }
 
 __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
-                                                    const int32_t* __restrict__ ids,
                                                     const uint32_t* __restrict__ bm,
                                                     const int32_t* __restrict__ wordoff,
                                                     const uint8_t* __restrict__ slot_of,
@@ -149,22 +162,7 @@ __global__ __launch_bounds__(256) void k_lists_fill(int T, int K, int E,
         const int j = __ffs((int)word) - 1;
         word &= word - 1;
         const int t = w * 32 + j;
-        if (slot_of) {  // the slot the top-K recorded for (t, e)
-            pairs[pos++] = t * K + slot_of[(size_t)t * E + e];
-            continue;
-        }
-        // the token's ids are loaded together (no chain of dependent loads); the first
-        // slot holding e is the one the bit stands for
-        const int32_t* row = ids + (size_t)t * K;
-        int32_t v[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = row[min(k, K - 1)];  // (unconditional loads)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = k < K ? v[k] : -1;
-        int kk = 0;
-#pragma unroll
-        for (int k = 15; k >= 0; --k) kk = v[k] == e ? k : kk;
-        pairs[pos++] = t * K + kk;
+        pairs[pos++] = t * K + slot_of[(size_t)t * E + e];  // the slot that chose (t, e)
     }
 }
 
@@ -372,11 +370,14 @@ hipError_t launch_lists(int T, int K, int E, int unit, const int32_t* ids, int32
     const int W = (T + 31) / 32;
     uint32_t* bm = (uint32_t*)scratch;
     int32_t* wordoff = (int32_t*)(bm + (size_t)W * E);
-    hipLaunchKernelGGL(k_lists_mark, dim3(W), dim3(256), 0, s, T, K, E, ids, bm);
+    // without the top-K's slot map the mark launch writes one into the scratch, so that the
+    // fill reads one byte a pair instead of the token's K ids
+    uint8_t* map = slot_of ? nullptr : lists_slot_map(scratch, T, E);
+    hipLaunchKernelGGL(k_lists_mark, dim3(W), dim3(256), 0, s, T, K, E, ids, bm, map);
     hipLaunchKernelGGL(k_lists_scan, dim3(1), dim3(1024), 0, s, T, K, E, unit, bm, wordoff,
                        counts, offsets, (int4*)units, num_units);
-    hipLaunchKernelGGL(k_lists_fill, dim3((W * E + 255) / 256), dim3(256), 0, s, T, K, E, ids, bm,
-                       wordoff, slot_of, pairs);
+    hipLaunchKernelGGL(k_lists_fill, dim3((W * E + 255) / 256), dim3(256), 0, s, T, K, E, bm,
+                       wordoff, slot_of ? slot_of : map, pairs);
     return hipGetLastError();
 }
 

@@ -515,8 +515,8 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     const int R = dyn ? static_passes(items, G) : 0x7fffffff, base = dyn ? 2 * R * G : 0;
     // Within the whole static blocks of 2G items, the two stages of a pass take two
     // neighbouring column tiles of one expert (a pass still covers one compact window of
-    // 2G items): for an expert of at most 16 tokens stage B then finds the group's
-    // activations already in LDS and loads none.  (Four tiles over two passes would skip
+    // 2G items): for an expert of at most 16 tokens (32 with two areas) stage B then finds
+    // the groups' activations already in LDS and loads none.  (Four tiles over two passes would skip
     // more loads, but hand a hot expert's heavy tiles to one workgroup four at a time:
     // measured slower with skewed routing.)  Items past those blocks (the dynamic tail, a
     // last partial block) keep their own order.

@@ -32,9 +32,8 @@ inline double side_share(int T, double share) { return T <= kNarrowSideTokens ? 
 // planned for three quarters of the GPU it takes 4 splits of 128-token chunks, not 5
 // (measured 495.7 -> 487.2 us per layer at 256 tokens)
 constexpr double kFrontShare = 0.75;
-// past this many tokens the shared expert is forked after the routing lists (see moe_layer);
-// up to it the expert passes end with a dynamic tail of work tickets
-constexpr int kLateForkTokens = kDynTailTokens;
+// past this many tokens the shared expert is forked after the routing lists (see moe_layer)
+constexpr int kLateForkTokens = 256;
 
 inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t up256(size_t b) { return (b + 255) / 256 * 256; }

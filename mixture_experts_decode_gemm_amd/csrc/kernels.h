@@ -46,13 +46,11 @@ hipError_t launch_ffn_mx(int T, int K, int E, int L, int I, int unit, const uint
                          const int32_t* units, const int32_t* num_units, void* rows,
                          uint8_t* hid, uint8_t* hid_scales, int stages, bool packed,
                          unsigned* counters, bool counters_zeroed, hipStream_t s);
-// Up to kDynTailTokens tokens the passes end with a dynamic tail of work tickets (the
-// layer then runs the shared expert's GEMMs beside them; see moe_layer), else every pass
-// is static.  counters: the two passes' work counters (16 words); counters_zeroed: the
-// caller's stream zeroed them since their last use (else the launcher zeroes them first
-// with a small kernel).  In moe_grouped_ffn's workspace they sit at ffn_counter_offset.
+// The passes end with a dynamic tail of work tickets.  counters: the two passes' work
+// counters (16 words); counters_zeroed: the caller's stream zeroed them since their last
+// use (else the launcher zeroes them first with a small kernel).  In moe_grouped_ffn's
+// workspace they sit at ffn_counter_offset.
 size_t ffn_counter_offset(int P, int I);
-constexpr int kDynTailTokens = 256;
 // From kUpTwoAreaTokens tokens the gate/up pass keeps two activation areas a wavefront
 // (an expert's second token group loaded ahead with its first); below, one (less LDS, so
 // that its workgroups share CUs with the side stream's GEMMs)

@@ -1,7 +1,8 @@
 """GPU parity of the routing front: router GEMM logits (tolerance, sampled rows of the
 1020-token workload), sigmoid top-16 fed identical FP32 logits (ids and weights
 bit-exact), routing lists and unit windows (bit-exact, every field), with uniform and
-Zipf-skewed bias, small ragged shapes, and dropped ids."""
+Zipf-skewed bias, small ragged shapes (the router GEMM with row-major and packed W_gate
+too), and dropped ids."""
 import numpy as np
 import pytest
 import torch
@@ -83,6 +84,32 @@ def test_router_front_1020(orc, zipf, packed):
     got = check_lists(orc, d, host(ids))
     D = int(np.count_nonzero(got["counts"]))
     say(f"  touched experts D={D}, units={got['num_units']}, max count={got['counts'].max()}")
+
+
+# the router GEMM and the top-K in one call at small ragged shapes: E = 96 (a multiple of
+# 32, not of 64: row-major W_gate only), E = 128 (also packed), T across chunk boundaries
+@pytest.mark.parametrize("T,E,K,packed", [(37, 96, 6, False), (129, 128, 8, False),
+                                          (129, 128, 8, True), (1, 128, 16, True)])
+def test_router_small_shapes(orc, T, E, K, packed):
+    H = 512
+    say(f"router T={T} E={E} K={K} packed={packed}")
+    x = syn.router_input(T, H, seed=T)
+    wg = syn.bf16_normal(syn.rng(T, 2), (E, H), 1 / np.sqrt(H))
+    bias = syn.routing_bias(E, 0, False)
+    d = moe.dims(T, T, hidden=H, experts=E, top_k=K)
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_router_workspace_size(d), dtype=torch.uint8, device="cuda")
+    wd = moe.moe_pack_dense_weight(dev(wg)) if packed else dev(wg)
+    moe.moe_router_topk(d, dev(x), wd, dev(bias), logits, ids, w,
+                        flags=moe.MOE_GATE_PACKED if packed else 0, workspace=ws)
+    torch.cuda.synchronize()
+    lg = host(logits)
+    assert_close(lg, orc.linear_f32(x, wg), "router logits (every row)")
+    rid, rw = orc.topk(lg, bias, K, 1, 2.5)  # on identical FP32 logits: bit-exact
+    assert np.array_equal(host(ids), rid)
+    assert np.array_equal(host(w).view(np.uint32), rw.view(np.uint32))
 
 
 @pytest.mark.parametrize("T,E,K,unit", [(8, 32, 4, 8), (37, 23, 6, 8), (130, 896, 16, 16),

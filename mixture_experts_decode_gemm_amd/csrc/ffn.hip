@@ -576,6 +576,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
         b = k + 1 < R ? b + 2 * G : ticket_item(base, ob.ticket);
         a = a_next;
     }
+    wait_vmcnt<0>();  // no direct load may still target LDS when the workgroup ends
 }
 
 // Up projection for any L % 128 == 0: wavefronts take K steps round-robin, weights are
@@ -889,6 +890,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
         a = a_next;
         b = b_next;
     }
+    wait_vmcnt<0>();  // no direct load may still target LDS when the workgroup ends
 }
 
 // Down projection for any I % 128 == 0 (weights loaded per K step)

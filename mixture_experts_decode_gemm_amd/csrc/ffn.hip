@@ -413,7 +413,7 @@ __device__ __forceinline__ UpOut up_group(UpStage<SPW>& st, const uint8_t* act, 
 // group's loads went out before the first group's (see up_issue_acts), so the second
 // group needs no wait; a third and later group (an expert of more than 32 tokens) loads
 // its activations into the second area and waits for every load in flight.
-template <int SPW, bool DUAL>
+template <int SPW, bool DUAL, int NV0 = up_weight_loads<SPW, DUAL>()>
 __device__ __forceinline__ UpOut up_compute(UpStage<SPW>& st, int K, int I, bool store,
                                             const uint8_t* __restrict__ codes, int cbytes,
                                             const uint8_t* __restrict__ scales,
@@ -423,7 +423,7 @@ __device__ __forceinline__ UpOut up_compute(UpStage<SPW>& st, int K, int I, bool
                                             int& rb, uint8_t* act, uint8_t* act1,
                                             int* tick = nullptr, int publish = 0) {
     const int r16 = threadIdx.x & 15;
-    UpOut first = up_group<SPW, up_weight_loads<SPW, DUAL>()>(
+    UpOut first = up_group<SPW, NV0>(
         st, act, 0, I, store, red + rb * RED_FLOATS, tick ? tick + rb : nullptr, publish);
     rb ^= 1;
     if (st.un.w <= 16) return first;
@@ -532,6 +532,16 @@ __global__ __launch_bounds__(256, 1) void k_ffn_up_fast(
     UpStage<SPW> A, B;
     // (B of A's expert: its groups are still in the areas up to this many tokens)
     constexpr int REUSE = DUAL ? 32 : 16;
+    if (items <= G) {  // (uniform) one item a workgroup: no second stage, no tickets; the
+                       // item's first group waits for every load (none follows them)
+        up_issue_weights<SPW, PACKED, DUAL>(A, a, nt, I, w13, s13, pairs, un_lds);
+        up_issue_acts<SPW, DUAL>(A, K, 0, codes, cbytes, scales, act, true, act1);
+        const UpOut o = up_compute<SPW, DUAL, 0>(A, K, I, true, codes, cbytes, scales, pairs,
+                                                 hid, hid_scales, red, rb, act, act1);
+        up_store(o, hid, hid_scales);
+        wait_vmcnt<0>();
+        return;
+    }
     up_issue_weights<SPW, PACKED, DUAL>(A, item_of(a), nt, I, w13, s13, pairs, un_lds);
     up_issue_acts<SPW, DUAL>(A, K, 0, codes, cbytes, scales, act, true, act1);
     // Items in pairs (stages A and B), pass k holding a_k and b_k.  Nothing between a
@@ -797,7 +807,7 @@ __device__ __forceinline__ void down_store(const DownStage<IS, MT>& st, int n0, 
 // conditional ticket, older).  The second group's hidden is already in hb1 (see
 // down_issue_acts); a third and later group reuses hb1 once every wavefront is done
 // reading it (a barrier ahead of its loads) and waits for every load in flight.
-template <int IS, int MT>
+template <int IS, int MT, int NV0 = down_weight_loads<IS, MT>()>
 __device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L, bool store,
                                              const uint8_t* __restrict__ hid, int hbytes,
                                              const uint8_t* __restrict__ hid_scales,
@@ -805,7 +815,7 @@ __device__ __forceinline__ void down_compute(DownStage<IS, MT>& st, int L, bool 
                                              uint16_t* __restrict__ rows, uint8_t* hb,
                                              uint8_t* hb1, uint8_t* stage) {
     const int r16 = threadIdx.x & 15;
-    down_mfma_stage<IS, MT, down_weight_loads<IS, MT>()>(st, hb, min(st.un.w, 16), stage);
+    down_mfma_stage<IS, MT, NV0>(st, hb, min(st.un.w, 16), stage);
     if (st.un.w <= 16) return;
     down_store(st, 0, L, store, rows, stage);
     st.pair = st.pair1;
@@ -850,6 +860,15 @@ __global__ __launch_bounds__(256, 1) void k_ffn_down_fast(
     const int R = dyn ? static_passes(items, G) : 0x7fffffff, base = dyn ? 2 * R * G : 0;
     int t_prev = 0;
     DownStage<IS, MT> A, B;
+    if (items <= G) {  // (uniform) one item a workgroup, as in the up projection
+        down_issue_weights<IS, MT, PACKED>(A, a, nt, L, w2, s2, pairs, un_lds);
+        down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0], hbuf1[0]);
+        down_compute<IS, MT, 0>(A, L, true, hid, hbytes, hid_scales, pairs, rows, hbuf[0],
+                                hbuf1[0], stage);
+        if (A.un.w <= 16) down_store(A, 0, L, true, rows, stage);
+        wait_vmcnt<0>();
+        return;
+    }
     down_issue_weights<IS, MT, PACKED>(A, a, nt, L, w2, s2, pairs, un_lds);
     down_issue_acts(A, 0, hid, hbytes, hid_scales, hbuf[0], hbuf1[0]);
     // items in pairs, nothing conditional between a stage's loads and its compute, each

@@ -36,8 +36,11 @@ def test_linear_small_int_exact(orc, M, N, K):
 
 
 # the weight-streaming path (K % 128 == 0, N % 32 == 0): one token, ragged 32-token tiles,
-# a second 256-token chunk that is partly empty, every token-tile count 1..8, split-K
-@pytest.mark.parametrize("M,N,K", [(1, 32, 128), (300, 224, 384), (510, 512, 1024),
+# a second 256-token chunk that is partly empty, every token-tile count 1..8, split-K; the
+# narrow batches of 1..8 tokens at the front GEMM's and the up-projection's shapes
+@pytest.mark.parametrize("M,N,K", [(1, 32, 128), (2, 96, 256), (3, 4480, 7168), (4, 64, 384),
+                                   (5, 7168, 3584), (8, 224, 640),
+                                   (300, 224, 384), (510, 512, 1024),
                                    (33, 4480, 7168), (97, 96, 256), (161, 64, 640),
                                    (200, 320, 896), (230, 128, 2048)])
 def test_linear_streaming_small_int_exact(orc, M, N, K):

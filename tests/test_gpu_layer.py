@@ -179,7 +179,8 @@ def test_full_layer_packed_equals_row_major():
     assert np.array_equal(out, out_ref)
 
 
-@pytest.mark.parametrize("T", [256, 65])
+# 8 and 1 tokens: the narrow batches' one-token-tile GEMM plans
+@pytest.mark.parametrize("T", [256, 65, 8, 1])
 def test_full_layer_dense_packed_equals_row_major(T):
     """moe_layer on packed dense weights (moe_pack_dense_weight) gives the row-major
     layer's output bit for bit; with the workspace intermediates equal too."""

@@ -41,6 +41,7 @@ DOWN_EXPERT_BYTES = 974_848        # W2 [3584, 512] MXFP4 + E8M0 scales
 WARM_FLOOR_S = 0.3                 # seconds of GPU work before the first timed layer step
 STAGE_FLOOR_S = 0.1                # the same before each other timed measurement
 ROTATE_SETS = 10                   # input sets rotated by the single-call timings (> 256 MB)
+SWEEP_MIN_STEPS = 200              # timed steps of each batch-sweep point, at least
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ffn_up_fast_T256_uniform_traffic.md")
 KERNEL_SOURCES = ["mixture_experts_decode_gemm_amd/csrc/ffn.hip",
@@ -404,7 +405,10 @@ def main():
         for name in ("uniform", "zipf"):
             weights = lw_with(biases[name])
             for t in (1, 8, 32, 64, 65, 130, 255, 256, 510, 1020):
-                st = run_T(t, a.steps, 3, STAGE_FLOOR_S, weights)
+                # at least SWEEP_MIN_STEPS timed steps a point (a narrow batch's step time
+                # varies from step to step: its shared expert and routed path take about as
+                # long), a few ms of GPU time each
+                st = run_T(t, max(a.steps, SWEEP_MIN_STEPS), 3, STAGE_FLOOR_S, weights)
                 m, Dt = st["ms"], st["D"]
                 bt = DENSE_BYTES + Dt * EXPERT_BYTES
                 pb = phase_bound_us(t, Dt)

@@ -82,6 +82,13 @@ __device__ __forceinline__ int winner_lane(bool hit, int cand_e) {
     return (int)__builtin_ctzll(__ballot(hit && ne == m));
 }
 
+// this lane's four bias values (experts j*256 + wave*64 + lane, clamped to E - 1)
+__device__ __forceinline__ void load_bias4(int E, const float* __restrict__ bias, float (&bi)[4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bi[j] = bias[min(j * 256 + wave * 64 + lane, E - 1)];
+}
+
 // One 256-thread workgroup per token.  Wavefront w owns experts w*64 + lane + 256 j
 // (j < 4, E <= 1024) with keys = order bits of the FP32 s + bias (0 where the lane has no
 // expert).  It finds its own top-K in K rounds: each lane offers its best remaining key
@@ -90,11 +97,13 @@ __device__ __forceinline__ int winner_lane(bool hit, int cand_e) {
 // winners (key, id, score) go to LDS; wavefront 0 then takes the 4K candidates, one a lane,
 // and picks the token's top-K from them the same way.  The order is that of one top-K over
 // all E keys: descending key, equal keys by ascending expert id.
-// lg: token t's E logits (global memory or LDS); cand_*: 64-entry LDS arrays.
+// lg: token t's E logits (global memory or LDS); bi: this lane's four bias values (experts
+// j*256 + wave*64 + lane, clamped to E - 1), loaded by the caller; cand_*: 64-entry LDS
+// arrays.
 // slot_of (optional, [T][E] bytes): slot_of[t][e] = the slot that chose expert e, for
 // the list build (entries of experts a token did not choose are left as they are).
 __device__ __forceinline__ void topk_token(int t, int E, int K, const float* lg,
-                                           const float* __restrict__ bias, int renorm,
+                                           const float (&bi)[4], int renorm,
                                            float scale, int32_t* __restrict__ ids,
                                            float* __restrict__ weights,
                                            uint8_t* __restrict__ slot_of, uint32_t* cand_key,
@@ -103,15 +112,11 @@ __device__ __forceinline__ void topk_token(int t, int E, int K, const float* lg,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t key[PER];
     float sc[PER];
-    // every logit and bias of this lane is loaded before the first use (clamped indices,
-    // no branches), so the wavefront waits for one round trip, not one per expert
-    float lgv[PER], bi[PER];
+    // every logit of this lane is loaded before the first use (clamped indices, no
+    // branches), so the wavefront waits for one round trip, not one per expert
+    float lgv[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int e = min(j * 256 + wave * 64 + lane, E - 1);
-        lgv[j] = lg[e];
-        bi[j] = bias[e];
-    }
+    for (int j = 0; j < PER; ++j) lgv[j] = lg[min(j * 256 + wave * 64 + lane, E - 1)];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = j * 256 + wave * 64 + lane;
@@ -194,7 +199,9 @@ __global__ __launch_bounds__(256) void k_topk(int T, int E, int K, const float* 
     __shared__ uint32_t cand_key[64];
     __shared__ int cand_e[64];
     __shared__ float cand_sc[64];
-    topk_token(blockIdx.x, E, K, src + (size_t)blockIdx.x * E, bias, renorm, scale, ids, weights,
+    float bi[4];
+    load_bias4(E, bias, bi);
+    topk_token(blockIdx.x, E, K, src + (size_t)blockIdx.x * E, bi, renorm, scale, ids, weights,
                slot_of, cand_key, cand_e, cand_sc);
 }
 
@@ -221,13 +228,15 @@ __global__ __launch_bounds__(256) void k_front_topk(int T, int N, int E, int L, 
     __shared__ float cand_sc[64];
     if ((int)blockIdx.x < T) {
         const int t = blockIdx.x;
+        float bi[4];
+        load_bias4(E, bias, bi);  // (in flight with the partials' loads)
         for (int c = threadIdx.x * 4; c < E; c += 1024) {
             const v4f v = sum_splits(part + (size_t)t * N + c, (size_t)T * N, S);
             *(v4f*)(lg + c) = v;
             *(v4f*)(logits + (size_t)t * E + c) = v;
         }
         __syncthreads();
-        topk_token(t, E, K, lg, bias, renorm, scale, ids, weights, slot_of, cand_key, cand_e,
+        topk_token(t, E, K, lg, bi, renorm, scale, ids, weights, slot_of, cand_key, cand_e,
                    cand_sc);
         return;
     }

@@ -353,13 +353,13 @@ hipError_t launch_wgemm(int M, int N, int N0, int N1, int K, const void* x, cons
 // the front GEMM), columns [N0, N1) -> out1 (row stride N1 - N0) with MODE 0 FP32, 1 BF16
 // (one rounding), 2 BF16 of FP32(add1) + sum; columns from N1 on are left to another
 // consumer.  Four columns per thread; the S partials are added in split order.
+// q: the four BF16 values of the added tensor at idx (MODE 2), loaded by the caller
 template <int MODE>
-__device__ __forceinline__ void store4(void* out, const void* add, size_t idx, v4f v) {
+__device__ __forceinline__ void store4(void* out, uint2 q, size_t idx, v4f v) {
     if (MODE == 0) {
         *(v4f*)((float*)out + idx) = v;
     } else {
         if (MODE == 2) {
-            const uint2 q = *(const uint2*)((const uint16_t*)add + idx);
             v[0] += bf16_lo(q.x);
             v[1] += bf16_hi(q.x);
             v[2] += bf16_lo(q.y);
@@ -379,11 +379,15 @@ __global__ __launch_bounds__(256) void k_wg_reduce(int M, int N, int N0, int N1,
     const int n4 = N1 / 4;
     if (idx >= (long)M * n4) return;
     const int m = (int)(idx / n4), c = (int)(idx - (long)m * n4) * 4;
+    const size_t i1 = (size_t)m * (N1 - N0) + (c >= N0 ? c - N0 : 0);
+    // the added values go out with the partials' loads (unconditionally, from a clamped
+    // index: a load behind a branch would be waited for on its own)
+    const uint2 q = MODE1 == 2 ? *(const uint2*)((const uint16_t*)add1 + i1) : make_uint2(0, 0);
     const v4f v = sum_splits(part + (size_t)m * N + c, (size_t)M * N, S);
     if (c < N0)
-        store4<0>(out0, nullptr, (size_t)m * N0 + c, v);
+        store4<0>(out0, q, (size_t)m * N0 + c, v);
     else
-        store4<MODE1>(out1, add1, (size_t)m * (N1 - N0) + (c - N0), v);
+        store4<MODE1>(out1, q, i1, v);
 }
 
 hipError_t launch_wg_reduce(int M, int N, int N0, int N1, int S, const float* parts, float* out0,
